@@ -1,0 +1,162 @@
+"""fp64 CPU oracle for the Gated DeltaNet replay / prefill path (TEST INFRASTRUCTURE).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py``
+may import this package.  It shares no code with the HIP library and never imports
+it; the product path must never reach it.
+
+The arithmetic lives in ``gdn_oracle.c`` (plain C, double precision, token by
+token).  This wrapper only widens inputs exactly to float64 and passes pointers.
+
+Pins (see ``tests/test_oracle_pins.py``): explicit-matrix brute force, exact
+rational arithmetic, closed forms (alpha=1/beta=0, single token, orthonormal keys
+with beta=1, repeated key overwrite), and invariants (alpha=0 makes replay equal
+prefill, the attenuation bound, split-prefill composition, r=L and r=0, GVA as
+duplicated heads, packing order).  No function here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+_lock = threading.Lock()
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with the host C compiler (gcc -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH) or \
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread",
+                               "-fno-fast-math", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB_PATH)
+            dp = ctypes.POINTER(ctypes.c_double)
+            ip = ctypes.POINTER(ctypes.c_int64)
+            i32, i64 = ctypes.c_int32, ctypes.c_int64
+            lib.gdn_oracle_prefill.argtypes = [i64, i32, i32, i32, i32, dp, dp, dp, dp, dp, ip,
+                                               dp, ctypes.c_double, dp, dp, i32]
+            lib.gdn_oracle_prefill.restype = ctypes.c_int
+            lib.gdn_oracle_replay.argtypes = [i64, i32, i32, i32, i32, dp, dp, dp, dp, dp, ip,
+                                              ip, ctypes.c_double, dp, dp, i32]
+            lib.gdn_oracle_replay.restype = ctypes.c_int
+            lib.gdn_oracle_state_relerr.argtypes = [dp, dp, i64, i64, dp]
+            lib.gdn_oracle_state_relerr.restype = ctypes.c_int64
+            _lib = lib
+    return _lib
+
+
+def widen(x) -> np.ndarray:
+    """Exact widening of a bf16 / fp32 / fp64 tensor or array to contiguous float64."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu")
+            if x.dtype == torch.bfloat16:
+                x = x.to(torch.float32)  # exact: every bf16 value is an fp32 value
+            return np.ascontiguousarray(x.numpy().astype(np.float64))
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _iptr(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def _threads(n):
+    if n is not None:
+        return int(n)
+    return int(os.environ.get("GDN_ORACLE_THREADS", os.cpu_count() or 1))
+
+
+def _common(q, k, v, g, beta, cu):
+    q, k, v, g, beta = (widen(a) for a in (q, k, v, g, beta))
+    cu = np.ascontiguousarray(np.asarray(cu, dtype=np.int64))
+    T, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    assert k.shape == q.shape and v.shape[0] == T and g.shape == (T, h_v) == beta.shape
+    assert cu[0] == 0 and cu[-1] == T
+    return q, k, v, g, beta, cu, h_qk, h_v, d_k, d_v
+
+
+def prefill(q, k, v, g, beta, cu_seqlens, S0=None, scale=1.0, want_o=True, threads=None):
+    """Full prefill from S0 (None = zero). Returns (S [N,h_v,d_k,d_v], o [T,h_v,d_v] or None)."""
+    q, k, v, g, beta, cu, h_qk, h_v, d_k, d_v = _common(q, k, v, g, beta, cu_seqlens)
+    N = len(cu) - 1
+    S = np.zeros((N, h_v, d_k, d_v), dtype=np.float64)
+    o = np.zeros((q.shape[0], h_v, d_v), dtype=np.float64) if want_o else None
+    s0 = widen(S0) if S0 is not None else None
+    if s0 is not None:
+        assert s0.shape == S.shape
+    rc = _load().gdn_oracle_prefill(N, h_qk, h_v, d_k, d_v, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                    _ptr(beta), _iptr(cu), _ptr(s0), float(scale), _ptr(S),
+                                    _ptr(o), _threads(threads))
+    if rc != 0:
+        raise ValueError("oracle prefill rejected its arguments")
+    return S, o
+
+
+def replay(q, k, v, g, beta, cu_seqlens, r, scale=1.0, want_o=True, threads=None):
+    """Tail replay from zero over the last r[n] tokens. Returns (S, o [sum r, h_v, d_v] or None)."""
+    q, k, v, g, beta, cu, h_qk, h_v, d_k, d_v = _common(q, k, v, g, beta, cu_seqlens)
+    N = len(cu) - 1
+    rr = np.ascontiguousarray(np.asarray(r, dtype=np.int64))
+    assert rr.shape == (N,)
+    S = np.zeros((N, h_v, d_k, d_v), dtype=np.float64)
+    o = np.zeros((int(rr.sum()), h_v, d_v), dtype=np.float64) if want_o else None
+    rc = _load().gdn_oracle_replay(N, h_qk, h_v, d_k, d_v, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                   _ptr(beta), _iptr(cu), _iptr(rr), float(scale), _ptr(S),
+                                   _ptr(o), _threads(threads))
+    if rc != 0:
+        raise ValueError("oracle replay rejected its arguments")
+    return S, o
+
+
+def state_relerr(A, B):
+    """Per-state ||A-B||_F/||B||_F (||A||_F if ||B||_F = 0) over the last two axes."""
+    A = widen(A); B = widen(B)
+    assert A.shape == B.shape and A.ndim >= 2
+    n_states = int(np.prod(A.shape[:-2])) if A.ndim > 2 else 1
+    elems = A.shape[-1] * A.shape[-2]
+    out = np.zeros(n_states, dtype=np.float64)
+    nf = _load().gdn_oracle_state_relerr(_ptr(A), _ptr(B), n_states, elems, _ptr(out))
+    return out.reshape(A.shape[:-2]) if A.ndim > 2 else out[0], int(nf)
+
+
+def chain_inputs(inp: dict, seq: int, head: int, window: str = "replay"):
+    """Slice one (sequence, v-head) chain's window out of packed inputs.
+
+    Returns (q, k, v, g, beta) with one sequence and one head each, as float64 arrays,
+    so the oracle can be run on a sample of a large workload.
+    """
+    w = inp["workload"]
+    cu = inp["cu_host"]; r = inp["r_host"]
+    hk = head * w.h_qk // w.h_v
+    end = int(cu[seq + 1])
+    start = end - int(r[seq]) if window == "replay" else int(cu[seq])
+    sl = slice(start, end)
+    return (widen(inp["q"][sl, hk:hk + 1]), widen(inp["k"][sl, hk:hk + 1]),
+            widen(inp["v"][sl, head:head + 1]), widen(inp["g"][sl, head:head + 1]),
+            widen(inp["beta"][sl, head:head + 1]))
