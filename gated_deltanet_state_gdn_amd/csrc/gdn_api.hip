@@ -1,0 +1,184 @@
+// C ABI of the library: host-side validation, workspace carving and launches.
+// Declarations and the contract of every entry point are in include/gdn.h.
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "../../include/gdn.h"
+#include "gdn_common.h"
+
+namespace {
+
+constexpr size_t kWorkspaceBytes = 256;   // status word, padded to one cache line
+
+bool aligned16(const void *p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+
+void debug(const char *msg)
+{
+    static const int on = [] {
+        const char *e = getenv("GDN_DEBUG");
+        return e && e[0] == '1';
+    }();
+    if (on) fprintf(stderr, "gdn: %s\n", msg);
+}
+
+int32_t check_desc(const gdn_desc *d, bool replay)
+{
+    if (!d) return GDN_ERR_NULL;
+    if (d->n_seqs < 0 || d->h_qk <= 0 || d->h_v <= 0 || d->d_k <= 0 || d->d_v <= 0 ||
+        d->total_tokens < 0 || d->total_out_tokens < 0) {
+        debug("negative or zero size in descriptor");
+        return GDN_ERR_SHAPE;
+    }
+    if (d->h_v % d->h_qk != 0) {
+        debug("h_v must be a multiple of h_qk");
+        return GDN_ERR_SHAPE;
+    }
+    if (!replay && d->total_out_tokens != d->total_tokens) {
+        debug("prefill writes one output row per token: total_out_tokens must equal total_tokens");
+        return GDN_ERR_SHAPE;
+    }
+    if (replay && d->total_out_tokens > d->total_tokens) {
+        debug("replay outputs cannot exceed the packed tokens");
+        return GDN_ERR_SHAPE;
+    }
+    if (d->total_tokens > 0x7fffffffLL) {
+        debug("more than 2^31-1 packed tokens");
+        return GDN_ERR_SHAPE;
+    }
+    if ((d->qkv_dtype != GDN_F32 && d->qkv_dtype != GDN_BF16) ||
+        (d->o_dtype != GDN_F32 && d->o_dtype != GDN_BF16)) {
+        debug("unknown dtype code");
+        return GDN_ERR_DTYPE;
+    }
+    if (d->o_dtype != d->qkv_dtype && d->o_dtype != GDN_F32) {
+        debug("o_dtype must equal qkv_dtype or be fp32");
+        return GDN_ERR_DTYPE;
+    }
+    const bool d_ok = (d->d_k == 64 || d->d_k == 128) && (d->d_v == 64 || d->d_v == 128);
+    if (!d_ok || (d->qkv_dtype == GDN_F32 && d->d_k != 64)) {
+        debug("unsupported head dims for this dtype");
+        return GDN_ERR_UNSUPPORTED;
+    }
+    return GDN_OK;
+}
+
+int32_t run(const gdn_desc *d, const void *q, const void *k, const void *v, const float *g,
+            const float *beta, const int32_t *cu, const int32_t *r, const float *S0, float *S_out,
+            void *o_out, int32_t *cu_out, void *ws, size_t ws_bytes, void *stream)
+{
+    const bool replay = r != nullptr;
+    int32_t st = check_desc(d, replay);
+    if (st != GDN_OK) return st;
+    if (!cu || !S_out || !ws) return GDN_ERR_NULL;
+    const bool any_tokens = d->total_tokens > 0;
+    if (any_tokens && (!q || !k || !v || !g || !beta)) return GDN_ERR_NULL;
+    if (o_out && d->total_out_tokens > 0 && !any_tokens) return GDN_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) ||
+        !aligned16(S0) || !aligned16(S_out) || !aligned16(o_out) || !aligned16(ws) ||
+        ((uintptr_t)cu & 3u) || ((uintptr_t)r & 3u) || ((uintptr_t)cu_out & 3u)) {
+        debug("pointer alignment: 16 bytes required (4 for integer arrays)");
+        return GDN_ERR_ALIGN;
+    }
+    if (ws_bytes < kWorkspaceBytes) return GDN_ERR_WORKSPACE;
+    if (d->n_seqs == 0) return GDN_OK;
+
+    gdn::ChunkArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.cu = cu; a.r = r; a.S0 = replay ? nullptr : S0;
+    a.S_out = S_out; a.o_out = o_out; a.cu_out = cu_out;
+    a.status = reinterpret_cast<int32_t *>(ws);
+    a.total_tokens = d->total_tokens;
+    a.total_out = d->total_out_tokens;
+    a.n_seqs = d->n_seqs; a.h_qk = d->h_qk; a.h_v = d->h_v;
+    a.o_f32 = (d->o_dtype == GDN_F32 && d->qkv_dtype == GDN_BF16) ? 1 : 0;
+    a.scale = d->scale;
+    const hipError_t e = gdn::launch_chunk(a, d->qkv_dtype == GDN_BF16, d->d_k, d->d_v,
+                                           o_out != nullptr, reinterpret_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported) return GDN_ERR_UNSUPPORTED;
+    return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char *gdn_status_str(int32_t s)
+{
+    switch (s) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL: return "required pointer is NULL";
+    case GDN_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case GDN_ERR_DTYPE: return "unknown or unsupported dtype combination";
+    case GDN_ERR_UNSUPPORTED: return "head dims / dtype not supported by this build";
+    case GDN_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+    case GDN_ERR_LAUNCH: return "kernel launch failed";
+    case GDN_ERR_DEVICE_INPUT: return "device-side cu_seqlens / r invalid";
+    case GDN_ERR_HIP: return "HIP runtime call failed";
+    default: return "unknown status";
+    }
+}
+
+int32_t gdn_replay_len(int32_t L, double rho)
+{
+    if (L <= 0 || !(rho > 0.0)) return 0;
+    const double x = rho * (double)L;
+    double c = ceil(x - 1e-9 * (x > 1.0 ? x : 1.0));
+    if (c < 0.0) c = 0.0;
+    if (c > (double)L) c = (double)L;
+    return (int32_t)c;
+}
+
+size_t gdn_workspace_bytes(const gdn_desc *desc)
+{
+    (void)desc;
+    return kWorkspaceBytes;
+}
+
+int32_t gdn_replay(const gdn_desc *d, const void *q, const void *k, const void *v, const float *g,
+                   const float *beta, const int32_t *cu_seqlens, const int32_t *r, float *S_out,
+                   void *o_out, int32_t *cu_out, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!r) return GDN_ERR_NULL;
+    return run(d, q, k, v, g, beta, cu_seqlens, r, nullptr, S_out, o_out, cu_out, ws, ws_bytes,
+               stream);
+}
+
+int32_t gdn_prefill(const gdn_desc *d, const void *q, const void *k, const void *v, const float *g,
+                    const float *beta, const int32_t *cu_seqlens, const float *S0, float *S_out,
+                    void *o_out, void *ws, size_t ws_bytes, void *stream)
+{
+    return run(d, q, k, v, g, beta, cu_seqlens, nullptr, S0, S_out, o_out, nullptr, ws, ws_bytes,
+               stream);
+}
+
+int32_t gdn_state_relerr(const float *S_a, const float *S_ref, int64_t n_states, int32_t d_k,
+                         int32_t d_v, float *relerr_out, int32_t *nonfinite_out, void *stream)
+{
+    if (n_states < 0 || d_k <= 0 || d_v <= 0) return GDN_ERR_SHAPE;
+    if ((int64_t)d_k * d_v % 4 != 0 || (int64_t)d_k * d_v > 0x7fffffffLL) return GDN_ERR_UNSUPPORTED;
+    if (n_states == 0) return GDN_OK;
+    if (!S_a || !S_ref || !relerr_out) return GDN_ERR_NULL;
+    if (!aligned16(S_a) || !aligned16(S_ref) || ((uintptr_t)relerr_out & 3u) ||
+        ((uintptr_t)nonfinite_out & 3u))
+        return GDN_ERR_ALIGN;
+    const hipError_t e = gdn::launch_relerr(S_a, S_ref, n_states, d_k * d_v, relerr_out,
+                                            nonfinite_out, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+int32_t gdn_device_status(const void *ws, void *stream, int32_t *status_host)
+{
+    if (!ws || !status_host) return GDN_ERR_NULL;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (hipStreamSynchronize(s) != hipSuccess) return GDN_ERR_HIP;
+    int32_t v = 0;
+    if (hipMemcpy(&v, ws, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return GDN_ERR_HIP;
+    *status_host = v;
+    return GDN_OK;
+}
+
+}  // extern "C"

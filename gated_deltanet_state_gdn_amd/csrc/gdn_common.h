@@ -1,0 +1,39 @@
+// Internal declarations shared by the C-ABI host code and the gfx950 kernels.
+// Not part of the public interface (that is include/gdn.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Arguments of the chunked gated-delta-rule kernel (one launch covers every
+// (sequence, v-head) chain of a call).
+struct ChunkArgs {
+    const void *q, *k, *v;      // [T, h_qk, d_k], [T, h_qk, d_k], [T, h_v, d_v]
+    const float *g, *beta;      // [T, h_v]
+    const int32_t *cu;          // [n_seqs + 1]
+    const int32_t *r;           // [n_seqs], replay lengths; nullptr = full prefill
+    const float *S0;            // [n_seqs, h_v, d_k, d_v] initial state (prefill), nullable
+    float *S_out;               // [n_seqs, h_v, d_k, d_v]
+    void *o_out;                // [T_out, h_v, d_v], nullable
+    int32_t *cu_out;            // [n_seqs + 1] output row offsets, nullable
+    int32_t *status;            // device status word (workspace)
+    int64_t total_tokens;
+    int64_t total_out;          // rows of o_out (bounds every o store)
+    int32_t n_seqs, h_qk, h_v;
+    int32_t o_f32;              // o stored as fp32 (1) or in the input dtype (0)
+    float scale;
+};
+
+// Launch the chunk kernel for the given dtype / head dims.  Returns hipSuccess or
+// the launch error; hipErrorNotSupported for an unsupported combination.
+hipError_t launch_chunk(const ChunkArgs &a, int bf16, int d_k, int d_v, bool with_o,
+                        hipStream_t stream);
+
+hipError_t launch_relerr(const float *A, const float *B, int64_t n_states, int32_t elems,
+                         float *relerr, int32_t *nonfinite, hipStream_t stream);
+
+constexpr int32_t kStatusOk = 0;
+constexpr int32_t kStatusBadInput = 8;   // == GDN_ERR_DEVICE_INPUT
+
+}  // namespace gdn

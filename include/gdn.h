@@ -1,0 +1,131 @@
+/*
+ * gdn.h -- C ABI of the Gated DeltaNet state-rebuild library for MI355X (gfx950).
+ *
+ * What the library computes.  Hybrid LLMs interleave full-attention layers with
+ * Gated DeltaNet linear-attention layers whose recurrent state cannot be rolled
+ * back to an arbitrary prefix boundary.  Tail-Replay (arXiv 2608.30310, abstract;
+ * gist.science technical summary, "Mecanismos Principais") rebuilds each
+ * linear-attention layer's state at a matched-prefix boundary by replaying only the
+ * most recent r tokens of the prefix, starting from a zero state, through the
+ * Gated DeltaNet recurrence.  Full prefill of the whole prefix is the baseline it
+ * is compared with (same pages, "Resultados").  Per (sequence, v-head):
+ *
+ *     S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = scale * S_t^T q_t,        alpha_t = exp(g_t),  g_t <= 0,
+ *
+ * with S a d_k x d_v matrix.  g = -inf is legal and means alpha = 0.
+ *
+ * Layouts (row-major, contiguous, packed varlen in "THD" order):
+ *     q, k       [T, h_qk, d_k]      in qkv_dtype
+ *     v          [T, h_v,  d_v]      in qkv_dtype
+ *     g, beta    [T, h_v]            fp32
+ *     cu_seqlens [n_seqs + 1]        int32, sequence n owns tokens [cu[n], cu[n+1])
+ *     r          [n_seqs]            int32 replay lengths, 0 <= r[n] <= cu[n+1]-cu[n]
+ *     S0, S_out  [n_seqs, h_v, d_k, d_v]  fp32
+ *     o_out      [T_out, h_v, d_v]   in o_dtype; rows packed per sequence in order
+ * v-head h reads q/k head floor(h * h_qk / h_v) (grouped value heads).
+ *
+ * Pointers are device pointers unless marked (host).  Every call is asynchronous
+ * on `stream` (a hipStream_t; NULL = the null stream) except gdn_device_status.
+ *
+ * Ownership: the caller owns every buffer, including the workspace.  The compute
+ * calls never allocate, free, synchronise or print, and keep no global mutable
+ * state; calls are re-entrant given distinct workspaces.
+ *
+ * Errors: problems checkable on the host (null required pointer, bad dims,
+ * h_v % h_qk != 0, unsupported d, misaligned pointer, small workspace) return a
+ * non-zero gdn_status before anything is enqueued.  A failed launch returns
+ * GDN_ERR_LAUNCH.  The device-resident cu_seqlens / r are validated by the kernel
+ * itself: on a bad value it records GDN_ERR_DEVICE_INPUT in the workspace status
+ * word (read it with gdn_device_status), skips the offending sequences and leaves
+ * their outputs unspecified.  Non-finite q/k/v/beta or g > 0 are not checked; the
+ * result is then undefined and gdn_state_relerr's non-finite count exposes it.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,          /* a required pointer is NULL */
+    GDN_ERR_SHAPE = 2,         /* negative / inconsistent sizes, h_v % h_qk != 0 */
+    GDN_ERR_DTYPE = 3,         /* unknown dtype code */
+    GDN_ERR_UNSUPPORTED = 4,   /* valid but not built: d_k, d_v outside {64,128}, fp32 with d_k = 128 */
+    GDN_ERR_ALIGN = 5,         /* a pointer is not 16-byte aligned */
+    GDN_ERR_WORKSPACE = 6,     /* workspace missing or smaller than gdn_workspace_bytes() */
+    GDN_ERR_LAUNCH = 7,        /* the HIP launch failed */
+    GDN_ERR_DEVICE_INPUT = 8,  /* device-side cu_seqlens / r invalid (from gdn_device_status) */
+    GDN_ERR_HIP = 9            /* a HIP runtime call failed (gdn_device_status only) */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef struct {
+    int32_t n_seqs;            /* packed sequences (a stack of independent layers may be packed as sequences) */
+    int32_t h_qk, h_v;         /* q/k heads and v heads, h_v % h_qk == 0 */
+    int32_t d_k, d_v;          /* head dims, each 64 or 128 */
+    int32_t qkv_dtype;         /* gdn_dtype of q, k, v */
+    int32_t o_dtype;           /* gdn_dtype of o: qkv_dtype, or GDN_F32 */
+    float scale;               /* o_t = scale * S_t^T q_t */
+    int64_t total_tokens;      /* T == cu_seqlens[n_seqs] (host copy) */
+    int64_t total_out_tokens;  /* rows of o_out: sum r[n] (replay) or T (prefill) */
+} gdn_desc;
+
+/* ABI version of the loaded library (GDN_ABI_VERSION). */
+int32_t gdn_abi_version(void);
+
+/* Static description of a status code. */
+const char *gdn_status_str(int32_t status);
+
+/* (host) Replay length for a matched prefix of L tokens under budget fraction rho:
+ * clamp(ceil(rho * L), 0, L) -- the pages replay the last 5-10 % of the matched
+ * prefix (Tail-Replay abstract; technical summary, "Resultados"). */
+int32_t gdn_replay_len(int32_t L, double rho);
+
+/* (host) Workspace bytes a call with this descriptor needs (>= 256, a status word). */
+size_t gdn_workspace_bytes(const gdn_desc *desc);
+
+/* Tail replay: for every sequence n and v-head h, run the recurrence from S = 0 over
+ * the last r[n] tokens [cu[n+1]-r[n], cu[n+1]) and write the state after the last
+ * token to S_out (the state at the prefix boundary; technical summary,
+ * "Reconstrucao de Estado Independente").  o_out (nullable) receives o_t for the
+ * replayed tokens, packed per sequence; cu_out (nullable, [n_seqs+1]) receives the
+ * output row offsets.  r[n] = 0 gives S = 0 (the pages' Zero-Only baseline) and no
+ * o rows; r[n] = L_n gives exactly gdn_prefill with S0 = NULL. */
+int32_t gdn_replay(const gdn_desc *desc, const void *q, const void *k, const void *v,
+                   const float *g, const float *beta, const int32_t *cu_seqlens,
+                   const int32_t *r, float *S_out, void *o_out, int32_t *cu_out,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Full prefill: the recurrence over every whole sequence from S0 (NULL = zero
+ * state).  o_out (nullable) has one row per token, in token order.  With S0 set to
+ * a rebuilt state it continues a prefix into its suffix. */
+int32_t gdn_prefill(const gdn_desc *desc, const void *q, const void *k, const void *v,
+                    const float *g, const float *beta, const int32_t *cu_seqlens,
+                    const float *S0, float *S_out, void *o_out,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Error report: relerr[s] = ||S_a[s] - S_ref[s]||_F / ||S_ref[s]||_F (||S_a[s]||_F when
+ * the reference is zero), fp64 accumulation; nonfinite[s] (nullable) counts the
+ * non-finite entries of S_a[s].  States are d_k x d_v fp32 blocks. */
+int32_t gdn_state_relerr(const float *S_a, const float *S_ref, int64_t n_states, int32_t d_k,
+                         int32_t d_v, float *relerr_out, int32_t *nonfinite_out, void *stream);
+
+/* (host, synchronising) Wait for `stream` and read the status word the last compute
+ * call that launched work wrote into `workspace`: GDN_OK or GDN_ERR_DEVICE_INPUT.
+ * GDN_ERR_HIP if the wait or the copy failed. */
+int32_t gdn_device_status(const void *workspace, void *stream, int32_t *status_host);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

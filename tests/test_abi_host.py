@@ -1,0 +1,107 @@
+"""Host-side checks of the C ABI (no GPU needed: no call here reaches a kernel).
+
+The library must load and export every entry point include/gdn.h declares, and
+every argument error checkable on the host must be reported before anything is
+enqueued.  Pointers below are fake non-NULL addresses that are never dereferenced:
+each call returns from host validation.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    import gated_deltanet_state_gdn_amd as gdn
+    if not os.path.exists(gdn.LIB_PATH):
+        pytest.skip("libgdn.so not built here")
+    return gdn, gdn.load()
+
+
+def test_header_declarations_are_exported():
+    gdn, lib = _lib()
+    hdr = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    declared = set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", hdr))
+    assert declared == set(gdn._lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_status_and_replay_len():
+    gdn, lib = _lib()
+    assert gdn.gdn_abi_version() == 1
+    for code in range(10):
+        assert gdn.gdn_status_str(code) not in ("unknown status", "")
+    for L in (0, 1, 7, 64, 100, 2048, 8192, 32768, 12345):
+        for rho in (0.0, 0.01, 0.02, 0.05, 0.07, 0.1, 0.2, 0.5, 1.0, 1.5):
+            assert gdn.gdn_replay_len(L, rho) == workloads.replay_len(L, rho), (L, rho)
+
+
+def _desc(gdn, **kw):
+    d = gdn._lib.GdnDesc()
+    base = dict(n_seqs=1, h_qk=2, h_v=4, d_k=128, d_v=128, qkv_dtype=1, o_dtype=1, scale=1.0,
+                total_tokens=100, total_out_tokens=10)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(d, k, v)
+    return d
+
+
+P = ctypes.c_void_p(0x100000)      # 16-byte aligned fake address
+PM = ctypes.c_void_p(0x100008)     # misaligned
+
+
+def _replay(lib, d, q=P, o=None, ws=P, ws_bytes=256, r=P, cu=P, S=P):
+    return lib.gdn_replay(ctypes.byref(d) if d is not None else None, q, P, P, P, P, cu, r, S, o,
+                          None, ws, ws_bytes, None)
+
+
+def test_host_validation_codes():
+    gdn, lib = _lib()
+    L = gdn._lib
+    assert _replay(lib, None) == L.GDN_ERR_NULL
+    assert _replay(lib, _desc(gdn, h_v=3)) == L.GDN_ERR_SHAPE
+    assert _replay(lib, _desc(gdn, n_seqs=-1)) == L.GDN_ERR_SHAPE
+    assert _replay(lib, _desc(gdn, total_out_tokens=101)) == L.GDN_ERR_SHAPE
+    assert _replay(lib, _desc(gdn, d_k=96)) == L.GDN_ERR_UNSUPPORTED
+    assert _replay(lib, _desc(gdn, d_v=256)) == L.GDN_ERR_UNSUPPORTED
+    assert _replay(lib, _desc(gdn, qkv_dtype=0, o_dtype=0)) == L.GDN_ERR_UNSUPPORTED  # fp32, d_k=128
+    assert _replay(lib, _desc(gdn, qkv_dtype=7)) == L.GDN_ERR_DTYPE
+    assert _replay(lib, _desc(gdn, qkv_dtype=0, o_dtype=1, d_k=64)) == L.GDN_ERR_DTYPE
+    assert _replay(lib, _desc(gdn), q=PM) == L.GDN_ERR_ALIGN
+    assert _replay(lib, _desc(gdn), o=PM) == L.GDN_ERR_ALIGN
+    assert _replay(lib, _desc(gdn), ws_bytes=16) == L.GDN_ERR_WORKSPACE
+    assert _replay(lib, _desc(gdn), ws=None) == L.GDN_ERR_NULL
+    assert _replay(lib, _desc(gdn), r=None) == L.GDN_ERR_NULL
+    assert _replay(lib, _desc(gdn), q=None) == L.GDN_ERR_NULL
+    assert _replay(lib, _desc(gdn), cu=None) == L.GDN_ERR_NULL
+    assert _replay(lib, _desc(gdn), S=None) == L.GDN_ERR_NULL
+    # nothing to do: accepted without a launch
+    assert _replay(lib, _desc(gdn, n_seqs=0)) == L.GDN_OK
+    # prefill: one output row per token
+    d = _desc(gdn)
+    assert lib.gdn_prefill(ctypes.byref(d), P, P, P, P, P, P, None, P, None, P, 256, None) == L.GDN_ERR_SHAPE
+    d = _desc(gdn, total_out_tokens=100, n_seqs=0)
+    assert lib.gdn_prefill(ctypes.byref(d), P, P, P, P, P, P, None, P, None, P, 256, None) == L.GDN_OK
+
+
+def test_relerr_and_status_validation():
+    gdn, lib = _lib()
+    L = gdn._lib
+    assert lib.gdn_state_relerr(P, P, -1, 128, 128, P, None, None) == L.GDN_ERR_SHAPE
+    assert lib.gdn_state_relerr(P, P, 0, 128, 128, P, None, None) == L.GDN_OK
+    assert lib.gdn_state_relerr(None, P, 3, 128, 128, P, None, None) == L.GDN_ERR_NULL
+    assert lib.gdn_state_relerr(PM, P, 3, 128, 128, P, None, None) == L.GDN_ERR_ALIGN
+    out = ctypes.c_int32(0)
+    assert lib.gdn_device_status(None, None, ctypes.byref(out)) == L.GDN_ERR_NULL
+    assert lib.gdn_device_status(P, None, None) == L.GDN_ERR_NULL
+
+
+def test_workspace_size():
+    gdn, lib = _lib()
+    assert gdn.gdn_workspace_bytes(_desc(gdn)) >= 256
