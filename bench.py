@@ -1,0 +1,226 @@
+"""Benchmark: Gated DeltaNet state rebuild by tail replay on one MI355X.
+
+Default workload: a stack of 36 independent GDN layers (16 q/k heads shared by 32
+v heads, d_k = d_v = 128, bf16 inputs, fp32 state), matched prefix L = 32768,
+replay budget 10 % (r = 3277), outputs o emitted.  The 36 layers' replays are
+independent (each layer has its own inputs and its own state), so one step is one
+gdn_replay call over the 36 layers packed as 36 sequences.
+
+Metric: replayed tokens per second per GDN layer (= 36 * r / step time) and the
+state-rebuild time per layer (step time / 36).  Inputs are resident in HBM when the
+timed region starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg2|cfg1|cfg4|cfg3]
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, 8 TB/s
+METRIC = "replayed tokens/s per GDN layer; state-rebuild µs at 32K prefix/10% replay"
+
+
+def algorithmic_bytes(w, tokens: int, n_states: int, with_o: bool) -> int:
+    """Bytes a call must move at minimum: q, k (q only with o), v, g, beta read once per
+    token; o written once per token; S written once per (sequence, v-head)."""
+    b = 2 if w.dtype == "bf16" else 4
+    per_tok = (2 if with_o else 1) * w.h_qk * w.d_k * b + w.h_v * w.d_v * b + 8 * w.h_v
+    if with_o:
+        per_tok += w.h_v * w.d_v * b
+    return tokens * per_tok + n_states * w.h_v * w.d_k * w.d_v * 4
+
+
+def algorithmic_flops(w, tokens: int, with_o: bool, C: int = 64) -> float:
+    """Chunked-form flops per token (C = 64): q/k Gram products per q/k head, and the
+    UT solve, pseudo-value, output and state products per v-head."""
+    o = 1 if with_o else 0
+    d = w.d_k
+    return tokens * (w.h_qk * (2 + 2 * o) * C * d + w.h_v * ((4 + 2 * o) * C * d + (4 + 2 * o) * d * d))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="cfg2")
+    ap.add_argument("--no-o", action="store_true", help="state only (no per-token outputs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-extra", action="store_true", help="skip prefill / per-layer timings")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus %d is not supported "
+                                   "(the path shards by (sequence, v-head) with no exchange, "
+                                   "see the design notes)" % args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_deltanet_state_gdn_amd as gdn
+    import workloads as W
+
+    gdn.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = {"cfg0": 0, "cfg1": 1, "cfg2": 2, "cfg3": 3, "cfg4": 4}[args.workload]
+    w = W.config(cfg)
+    with_o = not args.no_o
+    t_gen = time.time()
+    inp = W.make_inputs(w, device=dev)
+    torch.cuda.synchronize()
+    t_gen = time.time() - t_gen
+    q, k, v, g, beta = inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"]
+    cu, r = inp["cu_seqlens"], inp["r"]
+    n_seqs = len(inp["r_host"])
+    tot = int(inp["r_host"].sum())
+    desc = gdn.make_desc(q, v, n_seqs, tot, w.scale)
+    ws = gdn.workspace(desc, dev)
+    S = torch.empty((n_seqs, w.h_v, w.d_k, w.d_v), dtype=torch.float32, device=dev)
+    o = torch.empty((tot, w.h_v, w.d_v), dtype=q.dtype, device=dev) if with_o else None
+    stream = torch.cuda.current_stream()
+
+    def step():
+        gdn.gdn_replay(q, k, v, g, beta, cu, r, total_out_tokens=tot, S_out=S, o_out=o, ws=ws,
+                       scale=w.scale, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    status = gdn.gdn_device_status(ws, stream)
+    if status != 0:
+        raise RuntimeError("device status %d" % status)
+
+    # timed region: K steps, per-launch events on the launch stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    kern_ms = float(np.mean(launch_ms))
+
+    layers = n_seqs if w.layers > 1 else 1
+    # per GDN layer: a layer rebuilds r tokens in t_step / layers, so its throughput is
+    # (layers * r) / t_step = replayed tokens of the step over the step time.
+    value = tot / (ms_per_step * 1e-3)
+    abytes = algorithmic_bytes(w, tot, n_seqs, with_o)
+    aflops = algorithmic_flops(w, tot, with_o)
+    achieved = abytes / (kern_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "n_seqs": n_seqs, "h_qk": w.h_qk,
+                   "h_v": w.h_v, "d_k": w.d_k, "d_v": w.d_v, "L": list(w.lengths)[:4],
+                   "r": list(w.replay)[:4], "replayed_tokens_per_step": tot, "with_o": with_o,
+                   "state": "fp32"},
+        "rebuild_us_per_layer": kern_ms * 1e3 / layers,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": abytes, "kernel_ms": kern_ms,
+                     "algorithmic_tflops": aflops / (kern_ms * 1e-3) / 1e12},
+    }
+
+    if not args.no_extra:
+        # one layer per call (latency of a single layer's rebuild)
+        if w.layers > 1:
+            per = int(inp["cu_host"][1])
+            sl = slice(0, per)
+            r1 = r[:1]
+            cu1 = cu[:2]
+            o1 = torch.empty((int(inp["r_host"][0]), w.h_v, w.d_v), dtype=q.dtype, device=dev) if with_o else None
+            S1 = torch.empty((1, w.h_v, w.d_k, w.d_v), dtype=torch.float32, device=dev)
+            f1 = lambda: gdn.gdn_replay(q[sl], k[sl], v[sl], g[sl], beta[sl], cu1, r1,
+                                        total_out_tokens=int(inp["r_host"][0]), S_out=S1, o_out=o1,
+                                        ws=ws, scale=w.scale, stream=stream)
+            for _ in range(3):
+                f1()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(10):
+                f1()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out["single_layer_call_us"] = e0.elapsed_time(e1) * 1e3 / 10
+        # full prefill of the same packed prefixes (the baseline the replay replaces)
+        Sp = torch.empty_like(S)
+        op = torch.empty((int(q.shape[0]), w.h_v, w.d_v), dtype=q.dtype, device=dev) if with_o else None
+        fp = lambda: gdn.gdn_prefill(q, k, v, g, beta, cu, S_out=Sp, o_out=op, ws=ws,
+                                     scale=w.scale, stream=stream)
+        fp()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(3):
+            fp()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pms = e0.elapsed_time(e1) / 3
+        out["prefill_us_per_layer"] = pms * 1e3 / layers
+        out["prefill_over_replay"] = pms / kern_ms
+        rel, nf = gdn.gdn_state_relerr(S, Sp, stream=stream)
+        torch.cuda.synchronize()
+        out["relerr_replay_vs_full"] = {"max": float(rel.max()), "median": float(rel.median()),
+                                        "nonfinite": int(nf.sum())}
+        del op, Sp
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, with_o, args.cpu_seconds)
+
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, inp, with_o, budget_s):
+    """The fp64 oracle on this host's cores, on a bounded sample of the same workload:
+    whole layers (all v-heads of one packed sequence) replayed until ~budget_s seconds."""
+    import oracle
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    cu, r = inp["cu_host"], inp["r_host"]
+    done_tok, t_used, layers = 0, 0.0, 0
+    for n in range(len(r)):
+        end = int(cu[n + 1]); s = end - int(r[n])
+        sl = slice(s, end)
+        q, k, v = (oracle.widen(inp[x][sl]) for x in ("q", "k", "v"))
+        g, b = oracle.widen(inp["g"][sl]), oracle.widen(inp["beta"][sl])
+        t0 = time.perf_counter()
+        oracle.replay(q, k, v, g, b, [0, end - s], [end - s], scale=w.scale, want_o=with_o,
+                      threads=threads)
+        t_used += time.perf_counter() - t0
+        done_tok += end - s
+        layers += 1
+        if t_used >= budget_s:
+            break
+    return {"value": done_tok / t_used, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d packed sequences (layers), all %d v-heads, %d replayed tokens, "
+                      "fp64 token-by-token, %.1f s" % (layers, len(r), w.h_v, done_tok, t_used)}
+
+
+if __name__ == "__main__":
+    main()

@@ -30,6 +30,8 @@
 // lane group in B; the accumulator holds D[4*(l/16)+i][l%16] in element i.  A
 // fragment whose contraction indices follow the accumulator rows lets a D tile be
 // used directly as a B operand (S in K S, Y in T Y, U in P U and K^T U).
+#include <type_traits>
+
 #include "gdn_common.h"
 
 namespace gdn {
@@ -41,8 +43,6 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 constexpr int CH = 64;       // chunk length (tokens)
-constexpr int NWAVE = 4;
-constexpr int NTHR = 64 * NWAVE;
 constexpr int LDF = CH + 4;  // row stride of the fp32 64x64 scratch matrices
 constexpr int LDX = 16 + 4;  // row stride of a 16x16 fp32 scratch tile
 
@@ -146,6 +146,59 @@ __device__ __forceinline__ float ld_in(const uint16_t *p) { return bf2f(*p); }
 __device__ __forceinline__ void st_op(float *p, float x) { *p = x; }
 __device__ __forceinline__ void st_op(uint16_t *p, float x) { *p = f2bf(x); }
 
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(uint16_t x) { return bf2f(x); }
+
+// A fragment of T_off, the strictly-lower part of T (stored in LDS as fp32 with zeros
+// on and above the diagonal), converted to the operand type of the policy.
+template <class P>
+__device__ __forceinline__ typename P::Frag tfrag(const float *Tf, int r0, int kb, int lane) {
+    const int row = r0 + (lane & 15);
+    if constexpr (P::kBF16) {
+        const int k0 = kb * 32 + 4 * (lane >> 4);
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(Tf + row * LDF + k0);
+        const f32x4 y = *reinterpret_cast<const f32x4 *>(Tf + row * LDF + k0 + 16);
+        const u32x4 u = {pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(y[0], y[1]), pack2(y[2], y[3])};
+        return __builtin_bit_cast(bf16x8, u);
+    } else {
+        return *reinterpret_cast<const f32x4 *>(Tf + row * LDF + kb * 16 + 4 * (lane >> 4));
+    }
+}
+
+// V held in registers between its load and Y, one element per register.
+template <class P> struct VHold {
+    typedef typename std::conditional<P::kBF16, uint32_t, float>::type T;
+    static constexpr int N = 4;
+};
+
+// Rows r0..r0+3 of column col of v-head h; rows past the chunk end read the last valid
+// row (finite data that padded rows never use: their beta is 0).  No branches, so the
+// loads stay in flight until Y consumes them.
+template <class P>
+__device__ __forceinline__ void load_v_rows(typename VHold<P>::T *out, const typename P::E *vg,
+                                            int64_t t0, int r0, int len, int h_v, int h, int dv, int col) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = min(r0 + i, len - 1);
+        if constexpr (P::kBF16) out[i] = (uint32_t)vg[((t0 + row) * h_v + h) * dv + col];
+        else out[i] = vg[((t0 + row) * h_v + h) * dv + col];
+    }
+}
+template <class P>
+__device__ __forceinline__ float v_at(const typename VHold<P>::T *v, int i) {
+    if constexpr (P::kBF16) return __uint_as_float(v[i] << 16);
+    else return v[i];
+}
+
+// Workgroup barrier that orders LDS only: global loads stay in flight across it
+// (a full __syncthreads also waits for every outstanding global load).
+__device__ __forceinline__ void sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Lower-triangular 16x16 tile list of a 64x64 product (ti >= tj).
 __device__ __forceinline__ void tri_tile(int idx, int &ti, int &tj) {
     // 0:(0,0) 1:(1,0) 2:(1,1) 3:(2,0) 4:(2,1) 5:(2,2) 6:(3,0) 7:(3,1) 8:(3,2) 9:(3,3)
@@ -154,34 +207,43 @@ __device__ __forceinline__ void tri_tile(int idx, int &ti, int &tj) {
 }
 
 // ---------------------------------------------------------------- LDS plan
+// Four regions, reused across the phases of one chunk so that a workgroup needs
+// at most ~75 KB and two workgroups share a CU:
+//   K   K chunk, row-major                      (Gram, X = K S, source of K^T)
+//   Q   Q chunk, row-major; then O staging      (Gram, Q S; row-contiguous o store)
+//   T   T = (I + A)^{-1} fp32; then K^T (bf16)  (inversion, U = T Y; S update)
+//   P   A fp32 + inversion scratch; then P      (inversion; P U)
 template <int DK, int DV, int W, class P>
 struct Lds {
     typedef typename P::E E;
-    static constexpr int LDK = DK + P::PAD;    // K, Q rows
-    static constexpr int LDT = CH + P::PAD;    // K^T rows, T_off, P rows
-    static constexpr int LDV = W + P::PAD;     // V and O staging rows
-    static constexpr int oK = 0;
-    static constexpr int oQ = oK + CH * LDK * (int)sizeof(E);
-    static constexpr int oKt = oQ + CH * LDK * (int)sizeof(E);
-    static constexpr int nKt = P::kBF16 ? DK * LDT * (int)sizeof(E) : 0;
-    static constexpr int oV = oKt + nKt;
-    static constexpr int oT = oV + CH * LDV * (int)sizeof(E);
-    static constexpr int oPh = oT + CH * LDT * (int)sizeof(E);
-    static constexpr int oPl = oPh + CH * LDT * (int)sizeof(E);
-    static constexpr int nPl = P::kBF16 ? CH * LDT * (int)sizeof(E) : 0;
-    static constexpr int oAf = oPl + nPl;                        // A (fp32); O staging aliases it
-    static constexpr int nAf = CH * LDF * 4;
-    static constexpr int nOs = CH * (W + 4) * 4;                 // worst case fp32 staging
-    static constexpr int oTf = oAf + (nAf > nOs ? nAf : nOs);
-    static constexpr int oXs = oTf + CH * LDF * 4;
-    static constexpr int oGate = oXs + 4 * 16 * LDX * 4;
-    static constexpr int bytes = oGate + 8 * CH * 4 + 64;
+    static constexpr int LDK = DK + P::PAD;          // K, Q rows
+    static constexpr int LDO = W + P::PAD;           // O staging rows
+    static constexpr int LDKT = CH + 4;              // K^T rows (bf16)
+    static constexpr int LDP = CH + P::PAD;          // P rows
+    static constexpr int nK = CH * LDK * (int)sizeof(E);
+    static constexpr int nQ0 = CH * LDK * (int)sizeof(E);
+    static constexpr int nO = CH * LDO * (int)sizeof(E);
+    static constexpr int nQ = nQ0 > nO ? nQ0 : nO;
+    static constexpr int nT0 = CH * LDF * 4;
+    static constexpr int nKt = P::kBF16 ? DK * LDKT * 2 : 0;
+    static constexpr int nT = nT0 > nKt ? nT0 : nKt;
+    static constexpr int nA = CH * LDF * 4 + 4 * 16 * LDX * 4;          // A + 4 scratch tiles
+    static constexpr int nPP = (P::kBF16 ? 2 : 1) * CH * LDP * (int)sizeof(E);
+    static constexpr int nP = nA > nPP ? nA : nPP;
+    static constexpr int oG = 0;                     // gate arrays first: small offsets
+    static constexpr int oK = 6 * CH * 4 + 64;
+    static constexpr int oQ = oK + nK;
+    static constexpr int oT = oQ + nQ;
+    static constexpr int oP = oT + nT;
+    static constexpr int bytes = oP + nP;
 };
 
 // ---------------------------------------------------------------- kernel
 template <int DK, int DV, int W, class P, bool WITH_O>
-__global__ void __launch_bounds__(NTHR) gdn_chunk_kernel(ChunkArgs a)
+__global__ void __launch_bounds__(64 * (W / 16)) gdn_chunk_kernel(ChunkArgs a)
 {
+    constexpr int NWAVE = W / 16;          // one 16-column tile of S per wave
+    constexpr int NTHR = 64 * NWAVE;
     typedef typename P::E E;
     typedef typename P::Frag Frag;
     typedef Lds<DK, DV, W, P> L;
@@ -192,30 +254,29 @@ __global__ void __launch_bounds__(NTHR) gdn_chunk_kernel(ChunkArgs a)
     constexpr int KBT = CH / P::KB;        // k-blocks over the chunk's tokens
     constexpr int NCB = DV / W;            // column blocks per head
     static_assert(CT >= 1 && WC % 16 == 0, "wave column slab must be a multiple of 16");
+    static_assert(L::bytes <= 96 * 1024, "LDS plan");
 
     __shared__ __attribute__((aligned(16))) char smem[L::bytes];
     E *Ks = reinterpret_cast<E *>(smem + L::oK);
     E *Qs = reinterpret_cast<E *>(smem + L::oQ);
-    E *Kt = reinterpret_cast<E *>(smem + L::oKt);
-    E *Vs = reinterpret_cast<E *>(smem + L::oV);
-    E *Ts = reinterpret_cast<E *>(smem + L::oT);
-    E *Ph = reinterpret_cast<E *>(smem + L::oPh);
-    E *Pl = reinterpret_cast<E *>(smem + L::oPl);
-    float *Af = reinterpret_cast<float *>(smem + L::oAf);
-    E *Os = reinterpret_cast<E *>(smem + L::oAf);
-    float *Osf = reinterpret_cast<float *>(smem + L::oAf);
-    float *Tf = reinterpret_cast<float *>(smem + L::oTf);
-    float *Xs = reinterpret_cast<float *>(smem + L::oXs);
-    float *gG = reinterpret_cast<float *>(smem + L::oGate);   // raw g, then H
-    float *gE = gG + CH;       // e_i
+    E *Os = reinterpret_cast<E *>(smem + L::oQ);
+    float *Tf = reinterpret_cast<float *>(smem + L::oT);
+    uint16_t *Kt = reinterpret_cast<uint16_t *>(smem + L::oT);
+    float *Af = reinterpret_cast<float *>(smem + L::oP);
+    float *Xs = Af + CH * LDF;
+    E *Ph = reinterpret_cast<E *>(smem + L::oP);
+    E *Pl = Ph + CH * L::LDP;
+    float *gH = reinterpret_cast<float *>(smem + L::oG);   // cumulative log-gate since last reset
+    float *gE = gH + CH;       // e_i
     float *gB = gE + CH;       // beta_i
     float *gL = gB + CH;       // G_last,i
     float *gPd = gL + CH;      // (Q K^T)_ii
     int *gR = reinterpret_cast<int *>(gPd + CH);   // last reset index at or before i
     int64_t *gMisc = reinterpret_cast<int64_t *>(gR + CH);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lr = lane & 15, lg = lane >> 4;
+    const int tid0 = threadIdx.x, wave = tid0 >> 6;
+
+    int tid = tid0, lane = tid0 & 63, lr = lane & 15, lg = lane >> 4;
 
     // ---- block -> (sequence, v-head, column block); XCD-aware: consecutive logical
     // blocks (the v-heads of one q/k head, the heads of one sequence) share an XCD's L2.
@@ -293,89 +354,63 @@ __global__ void __launch_bounds__(NTHR) gdn_chunk_kernel(ChunkArgs a)
     const E *vg = reinterpret_cast<const E *>(a.v);
     constexpr int VEC = 16 / (int)sizeof(E);   // elements per 16-byte vector
     constexpr int NVK = DK / VEC;              // vectors per K/Q row
-    constexpr int NVV = W / VEC;               // vectors per V row (this column block)
-    static_assert(NVK <= 64 && NVV <= 64 && (64 % NVK) == 0 && (64 % NVV) == 0, "vector map");
+    constexpr int NVO = W / VEC;               // vectors per O row (this column block)
+    static_assert(NVK <= 64 && (64 % NVK) == 0 && (256 % NVO) == 0, "vector map");
+
+    constexpr int RPP = NTHR / NVK;            // K/Q rows per pass of the workgroup
+    constexpr int NPF = CH / RPP;              // passes per chunk
+    u32x4 kpf[NPF], qpf[NPF];
+    float gpf = 0.f, bpf = 0.f;
+    bool gok = false;
+    typename VHold<P>::T vnext[4][CT][VHold<P>::N];
+    auto fetch = [&](int64_t cc) {
+        const int ln = (int)((rn - cc) < CH ? (rn - cc) : CH);
+        const int64_t tb = wbeg + cc;
+        // rows past the chunk end load the last valid row: finite, and inert because
+        // their g and beta are set to 0 (alpha = 1, no write)
+#pragma unroll
+        for (int p = 0; p < NPF; ++p) {
+            const int row = min(p * RPP + tid / NVK, ln - 1);
+            const int64_t off = ((tb + row) * a.h_qk + hk) * DK + (int64_t)(tid % NVK) * VEC;
+            kpf[p] = *reinterpret_cast<const u32x4 *>(kg + off);
+            if (WITH_O) qpf[p] = *reinterpret_cast<const u32x4 *>(qg + off);
+        }
+        {
+            const int64_t off = (tb + min(lane, ln - 1)) * a.h_v + h;
+            gpf = a.g[off];
+            bpf = a.beta[off];
+            gok = lane < ln;
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+                load_v_rows<P>(vnext[tt][ct], vg, tb, 16 * tt + 4 * lg, ln, a.h_v, h, DV, col0 + 16 * ct + lr);
+    };
+    if (rn > 0) fetch(0);
 
     for (int64_t c0 = 0; c0 < rn; c0 += CH) {
         const int len = (int)((rn - c0) < CH ? (rn - c0) : CH);
         const int64_t t0 = wbeg + c0;
-        __syncthreads();
+        // lane-derived indices are recomputed each chunk instead of being held in
+        // registers across the whole loop
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+        sync_lds();
 
-        // ================= load the chunk (rows >= len are zero; g = 0, b = 0 there)
-        {
-            constexpr int RPP = NTHR / NVK;            // rows per pass
-            const int vc = tid % NVK, rsub = tid / NVK;
+        // ================= chunk inputs (prefetched during the previous chunk's state pass)
+        // into LDS.  Rows >= len repeat the last token's q/k/v but get g = 0 and beta = 0:
+        // a token with alpha = 1 and no write leaves S unchanged, and its pseudo-value is 0
 #pragma unroll
-            for (int p = 0; p < CH / RPP; ++p) {
-                const int row = p * RPP + rsub;
-                u32x4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
-                if (row < len) {
-                    const int64_t off = ((t0 + row) * a.h_qk + hk) * DK + (int64_t)vc * VEC;
-                    kv = *reinterpret_cast<const u32x4 *>(kg + off);
-                    if (WITH_O) qv = *reinterpret_cast<const u32x4 *>(qg + off);
-                }
-                *reinterpret_cast<u32x4 *>(Ks + row * L::LDK + vc * VEC) = kv;
-                if (WITH_O) *reinterpret_cast<u32x4 *>(Qs + row * L::LDK + vc * VEC) = qv;
-                if constexpr (P::kBF16) {
-                    // K^T: pack token pairs (2m, 2m+1) of one d_k index into a dword.
-                    // Partner row is NVK lanes away (same wave since NVK <= 32).
-                    const bool odd = (row & 1) != 0;
-                    const uint32_t s0 = odd ? kv.x : kv.z, s1 = odd ? kv.y : kv.w;
-                    const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, NVK);
-                    const uint32_t r1 = (uint32_t)__shfl_xor((int)s1, NVK);
-                    const int rev = row & ~1;
-                    uint32_t w0, w1, w2, w3;
-                    int e0;
-                    if (!odd) {   // my elements 0..3 (row 2m) + partner's 0..3 (row 2m+1)
-                        w0 = (kv.x & 0xffffu) | (r0 << 16);
-                        w1 = (kv.x >> 16) | (r0 & 0xffff0000u);
-                        w2 = (kv.y & 0xffffu) | (r1 << 16);
-                        w3 = (kv.y >> 16) | (r1 & 0xffff0000u);
-                        e0 = 0;
-                    } else {      // partner's elements 4..7 (row 2m) + my 4..7 (row 2m+1)
-                        w0 = (r0 & 0xffffu) | (kv.z << 16);
-                        w1 = (r0 >> 16) | (kv.z & 0xffff0000u);
-                        w2 = (r1 & 0xffffu) | (kv.w << 16);
-                        w3 = (r1 >> 16) | (kv.w & 0xffff0000u);
-                        e0 = 4;
-                    }
-                    const int dk0 = vc * VEC + e0;
-                    *reinterpret_cast<uint32_t *>(Kt + (dk0 + 0) * L::LDT + rev) = w0;
-                    *reinterpret_cast<uint32_t *>(Kt + (dk0 + 1) * L::LDT + rev) = w1;
-                    *reinterpret_cast<uint32_t *>(Kt + (dk0 + 2) * L::LDT + rev) = w2;
-                    *reinterpret_cast<uint32_t *>(Kt + (dk0 + 3) * L::LDT + rev) = w3;
-                }
-            }
+        for (int p = 0; p < NPF; ++p) {
+            const int row = p * RPP + tid / NVK;
+            *reinterpret_cast<u32x4 *>(Ks + row * L::LDK + (tid % NVK) * VEC) = kpf[p];
+            if (WITH_O) *reinterpret_cast<u32x4 *>(Qs + row * L::LDK + (tid % NVK) * VEC) = qpf[p];
         }
-        {
-            constexpr int RPP = NTHR / NVV;
-            const int vc = tid % NVV, rsub = tid / NVV;
-#pragma unroll
-            for (int p = 0; p < CH / RPP; ++p) {
-                const int row = p * RPP + rsub;
-                u32x4 vv = {0u, 0u, 0u, 0u};
-                if (row < len) {
-                    const int64_t off = ((t0 + row) * a.h_v + h) * DV + (int64_t)cb * W + vc * VEC;
-                    vv = *reinterpret_cast<const u32x4 *>(vg + off);
-                }
-                *reinterpret_cast<u32x4 *>(Vs + row * L::LDV + vc * VEC) = vv;
-            }
-        }
-        if (tid < CH) {
-            float gv = 0.f, bv = 0.f;
-            if (tid < len) {
-                const int64_t off = (t0 + tid) * a.h_v + h;
-                gv = a.g[off];
-                bv = a.beta[off];
-            }
-            gG[tid] = gv;
-            gB[tid] = bv;
-        }
-        __syncthreads();
-
-        // ================= gates (wave 0): reset-aware segmented scan over the chunk
         if (wave == 0) {
-            const float gv = gG[lane];
+            const float gv = gok ? gpf : 0.f, bv = gok ? bpf : 0.f;
+            // reset-aware inclusive scan: H = sum of g since the last alpha = 0 token
             const bool reset = gv == -__builtin_inff();
             float hv = reset ? 0.f : gv;
             int seg = reset ? 1 : 0;
@@ -393,77 +428,43 @@ __global__ void __launch_bounds__(NTHR) gdn_chunk_kernel(ChunkArgs a)
             }
             const float hl = __shfl(hv, 63);
             const int rl = __shfl(rho, 63);
-            gG[lane] = hv;
+            gH[lane] = hv;
             gE[lane] = rho < 0 ? __expf(hv) : 0.f;
+            gB[lane] = bv;
             gR[lane] = rho;
             gL[lane] = rl <= lane ? __expf(hl - hv) : 0.f;
         }
+        sync_lds();
 
-        // ================= Gram tiles: K K^T (tiles 0..9) and Q K^T (tiles 10..19)
-        constexpr int NG = WITH_O ? 20 : 10;
-        constexpr int GPW = (NG + NWAVE - 1) / NWAVE;
-        f32x4 gram[GPW];
+        // ================= A = strict_lower(diag(b) (K K^T o G))
+        // G_rc = exp(H_r - H_c) when no reset in (c, r]
 #pragma unroll
-        for (int j = 0; j < GPW; ++j) {
+        for (int j = 0; j < (10 + NWAVE - 1) / NWAVE; ++j) {
             const int idx = wave + NWAVE * j;
-            gram[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (idx < NG) {
+            if (idx < 10) {
                 int ti, tj;
-                tri_tile(idx % 10, ti, tj);
-                const E *Am = idx < 10 ? Ks : Qs;
+                tri_tile(idx, ti, tj);
+                f32x4 gr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < KBK; ++kb)
-                    gram[j] = mma(gram[j], frag_rows(Am, L::LDK, 16 * ti, kb, lane),
-                                  frag_rows(Ks, L::LDK, 16 * tj, kb, lane));
-            }
-        }
-        __syncthreads();
-
-        // ================= A = strict_lower(diag(b) (K K^T o G)); P = lower(Q K^T o G)
-#pragma unroll
-        for (int j = 0; j < GPW; ++j) {
-            const int idx = wave + NWAVE * j;
-            if (idx < NG) {
-                int ti, tj;
-                tri_tile(idx % 10, ti, tj);
+                    gr = mma(gr, frag_rows(Ks, L::LDK, 16 * ti, kb, lane), frag_rows(Ks, L::LDK, 16 * tj, kb, lane));
                 const int c = 16 * tj + lr;
-                const float hc = gG[c];
+                const float hc = gH[c];
+                const f32x4 hr = *reinterpret_cast<const f32x4 *>(gH + 16 * ti + 4 * lg);
+                const f32x4 br = *reinterpret_cast<const f32x4 *>(gB + 16 * ti + 4 * lg);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int rr = 16 * ti + 4 * lg + i;
-                    const float gam = (c <= rr && gR[rr] <= c) ? __expf(gG[rr] - hc) : 0.f;
-                    const float x = gram[j][i];
-                    if (idx < 10) {
-                        Af[rr * LDF + c] = c < rr ? gB[rr] * gam * x : 0.f;
-                    } else {
-                        const float pv = c < rr ? gam * x : 0.f;
-                        if constexpr (P::kBF16) {
-                            const uint16_t hb = f2bf(pv);
-                            Ph[rr * L::LDT + c] = hb;
-                            Pl[rr * L::LDT + c] = f2bf(pv - bf2f(hb));
-                        } else {
-                            Ph[rr * L::LDT + c] = pv;
-                        }
-                        if (c == rr) gPd[rr] = x;
-                    }
+                    const float gam = (c < rr && gR[rr] <= c) ? __expf(hr[i] - hc) : 0.f;
+                    Af[rr * LDF + c] = br[i] * gam * gr[i];
                 }
             }
-        }
-        if (WITH_O && P::kBF16 && wave < 2) {
-            // zero the upper tiles (0,1) and (2,3) read by 32-wide k-blocks of P
-            const int ti = 2 * wave, tj = ti + 1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rr = 16 * ti + 4 * lg + i, c = 16 * tj + lr;
-                Ph[rr * L::LDT + c] = 0;
-                Pl[rr * L::LDT + c] = 0;
             }
-        }
-        __syncthreads();
+        sync_lds();
 
         // ================= T = (I + A)^{-1} in fp32 (blocked, 16x16 diagonal blocks)
         // level 0: wave b inverts diagonal block b by forward substitution (column = lane)
-        if (lane < 16) {
+        if (wave < 4 && lane < 16) {
             const int b0 = 16 * wave;
             const int c = lane;
             float t[16];
@@ -473,11 +474,11 @@ __global__ void __launch_bounds__(NTHR) gdn_chunk_kernel(ChunkArgs a)
 #pragma unroll
                 for (int j = 0; j < i; ++j) s = fmaf(Af[(b0 + i) * LDF + b0 + j], t[j], s);
                 t[i] = i < c ? 0.f : (i == c ? 1.f : -s);
-            }
+                    }
 #pragma unroll
             for (int i = 0; i < 16; ++i) Tf[(b0 + i) * LDF + b0 + c] = t[i];
         }
-        __syncthreads();
+        sync_lds();
         // level 1: T_{b+1,b} = -T_{b+1,b+1} A_{b+1,b} T_{b,b} for b = 0 (wave 0), 2 (wave 1)
         if (wave < 2) {
             const int b = 2 * wave;
@@ -488,10 +489,10 @@ __global__ void __launch_bounds__(NTHR) gdn_chunk_kernel(ChunkArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i) Tf[(16 * (b + 1) + 4 * lg + i) * LDF + 16 * b + lr] = -y[i];
         }
-        __syncthreads();
+        sync_lds();
         // level 2: lower-left 32x32 block = -T_lowerright A_21 T_upperleft
-        const int la = wave >> 1, lb = wave & 1;
-        {
+        if (wave < 4) {
+            const int la = wave >> 1, lb = wave & 1;
             f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < 2; ++c)
@@ -502,8 +503,9 @@ __global__ void __launch_bounds__(NTHR) gdn_chunk_kernel(ChunkArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i) X[(4 * lg + i) * LDX + lr] = x[i];
         }
-        __syncthreads();
-        {
+        sync_lds();
+        if (wave < 4) {
+            const int la = wave >> 1, lb = wave & 1;
             f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int d = 0; d < 2; ++d)
@@ -513,63 +515,133 @@ __global__ void __launch_bounds__(NTHR) gdn_chunk_kernel(ChunkArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i) Tf[(16 * (2 + la) + 4 * lg + i) * LDF + 16 * lb + lr] = -y[i];
         }
-        __syncthreads();
-        // strictly lower part of T -> operand type (zeros elsewhere)
-        for (int e = tid; e < CH * CH; e += NTHR) {
+        // T_off keeps only the strictly-lower part: clear the diagonal and above
+        // (entries no wave writes in this phase)
+#pragma unroll
+        for (int j = 0; j < CH * CH / NTHR; ++j) {
+            const int e = tid + j * NTHR;
             const int rr = e >> 6, c = e & 63;
-            st_op(Ts + rr * L::LDT + c, c < rr ? Tf[rr * LDF + c] : 0.f);
+            if (c >= rr) Tf[rr * LDF + c] = 0.f;
         }
-        __syncthreads();
+        sync_lds();
+
+        // ================= P = strict_lower(Q K^T o G) and its diagonal (Q K^T)_ii
+        if constexpr (WITH_O) {
+#pragma unroll
+            for (int j = 0; j < (10 + NWAVE - 1) / NWAVE; ++j) {
+                const int idx = wave + NWAVE * j;
+                if (idx < 10) {
+                    int ti, tj;
+                    tri_tile(idx, ti, tj);
+                    f32x4 gr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kb = 0; kb < KBK; ++kb)
+                        gr = mma(gr, frag_rows(Qs, L::LDK, 16 * ti, kb, lane), frag_rows(Ks, L::LDK, 16 * tj, kb, lane));
+                    const int c = 16 * tj + lr;
+                    const float hc = gH[c];
+                    const f32x4 hr = *reinterpret_cast<const f32x4 *>(gH + 16 * ti + 4 * lg);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int rr = 16 * ti + 4 * lg + i;
+                        const float pv = (c < rr && gR[rr] <= c) ? __expf(hr[i] - hc) * gr[i] : 0.f;
+                        if constexpr (P::kBF16) {
+                            const uint16_t hb = f2bf(pv);
+                            Ph[rr * L::LDP + c] = hb;
+                            Pl[rr * L::LDP + c] = f2bf(pv - bf2f(hb));
+                        } else {
+                            Ph[rr * L::LDP + c] = pv;
+                        }
+                        if (c == rr) gPd[rr] = gr[i];
+                    }
+                }
+                    }
+            if (P::kBF16 && wave < 2) {
+                // zero the upper tiles (0,1) and (2,3) that 32-wide k-blocks of P read
+                const int ti = 2 * wave, tj = ti + 1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rr = 16 * ti + 4 * lg + i, c = 16 * tj + lr;
+                    Ph[rr * L::LDP + c] = 0;
+                    Pl[rr * L::LDP + c] = 0;
+                }
+            }
+            sync_lds();
+        }
 
         // ================= state pass on this wave's columns
         const float gam_c = gE[CH - 1];
-        // S fragments (hi and lo) over d_k
-        Frag sh[KBK][CT], sl[KBK][CT];
-#pragma unroll
-        for (int kb = 0; kb < KBK; ++kb)
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                if constexpr (P::kBF16) bfrag_split(S[2 * kb][ct], S[2 * kb + 1][ct], sh[kb][ct], sl[kb][ct]);
-                else sh[kb][ct] = S[kb][ct];
-            }
-        // X = K S ; Y = b (V - e X)
-        f32x4 Y[4][CT];
+        // X = K S (S as hi bf16) and Q S (S as hi + lo), k-block by k-block
+        f32x4 X[4][CT], QS[4][CT];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-                f32x4 x = {0.f, 0.f, 0.f, 0.f};
+                X[tt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                QS[tt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
-                for (int kb = 0; kb < KBK; ++kb) x = mma(x, frag_rows(Ks, L::LDK, 16 * tt, kb, lane), sh[kb][ct]);
+        for (int kb = 0; kb < KBK; ++kb) {
+            Frag sh[CT], sl[CT];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rr = 16 * tt + 4 * lg + i;
-                    const float vv = ld_in(Vs + rr * L::LDV + wave * WC + 16 * ct + lr);
-                    Y[tt][ct][i] = gB[rr] * (vv - gE[rr] * x[i]);
+            for (int ct = 0; ct < CT; ++ct) {
+                if constexpr (P::kBF16) bfrag_split(S[2 * kb][ct], S[2 * kb + 1][ct], sh[ct], sl[ct]);
+                else sh[ct] = S[kb][ct];
+            }
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const Frag kf = frag_rows(Ks, L::LDK, 16 * tt, kb, lane);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) X[tt][ct] = mma(X[tt][ct], kf, sh[ct]);
+                if constexpr (WITH_O) {
+                    const Frag qf = frag_rows(Qs, L::LDK, 16 * tt, kb, lane);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) {
+                        QS[tt][ct] = mma(QS[tt][ct], qf, sh[ct]);
+                        if constexpr (P::kBF16) QS[tt][ct] = mma(QS[tt][ct], qf, sl[ct]);
+                    }
                 }
             }
-        // U = Y + T_off Y
-        Frag yf[KBT][CT];
-#pragma unroll
-        for (int kb = 0; kb < KBT; ++kb)
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                if constexpr (P::kBF16) yf[kb][ct] = bfrag_hi(Y[2 * kb][ct], Y[2 * kb + 1][ct]);
-                else yf[kb][ct] = Y[kb][ct];
             }
-        f32x4 U[4][CT];
+        // Y = b (V - e X), in place
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            const int kmax = P::kBF16 ? tt / 2 : tt;
+            const f32x4 br = *reinterpret_cast<const f32x4 *>(gB + 16 * tt + 4 * lg);
+            const f32x4 er = *reinterpret_cast<const f32x4 *>(gE + 16 * tt + 4 * lg);
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                U[tt][ct] = Y[tt][ct];
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                for (int kb = 0; kb < KBT; ++kb)
-                    if (kb <= kmax) U[tt][ct] = mma(U[tt][ct], frag_rows(Ts, L::LDT, 16 * tt, kb, lane), yf[kb][ct]);
+                for (int i = 0; i < 4; ++i)
+                    X[tt][ct][i] = br[i] * (v_at<P>(vnext[tt][ct], i) - er[i] * X[tt][ct][i]);
+        }
+        // every input of this chunk is consumed: fetch the next chunk's, which land while
+        // the rest of this chunk is processed
+        if (c0 + CH < rn) fetch(c0 + CH);
+        // U = Y + T_off Y  (unit diagonal exact; T_off read from the fp32 inverse)
+        f32x4 U[4][CT];
+        {
+            Frag yf[KBT][CT];
+#pragma unroll
+            for (int kb = 0; kb < KBT; ++kb)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    if constexpr (P::kBF16) yf[kb][ct] = bfrag_hi(X[2 * kb][ct], X[2 * kb + 1][ct]);
+                    else yf[kb][ct] = X[kb][ct];
+                }
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) U[tt][ct] = X[tt][ct];
+#pragma unroll
+                for (int kb = 0; kb < KBT; ++kb) {
+                    if (kb * P::KB < 16 * tt + 16) {
+                        const Frag tf = tfrag<P>(Tf, 16 * tt, kb, lane);
+#pragma unroll
+                        for (int ct = 0; ct < CT; ++ct) U[tt][ct] = mma(U[tt][ct], tf, yf[kb][ct]);
+                    }
+                }
             }
         }
-        // U fragments for the output product
+        // O = e (Q S) + Pd U + P_off U   (QS registers become O)
         if constexpr (WITH_O) {
             Frag uh[KBT][CT], ul[KBT][CT];
 #pragma unroll
@@ -579,101 +651,135 @@ __global__ void __launch_bounds__(NTHR) gdn_chunk_kernel(ChunkArgs a)
                     if constexpr (P::kBF16) bfrag_split(U[2 * kb][ct], U[2 * kb + 1][ct], uh[kb][ct], ul[kb][ct]);
                     else uh[kb][ct] = U[kb][ct];
                 }
-            // O = e (Q S) + Pd U + P_off U
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
-                const int kmax = P::kBF16 ? tt / 2 : tt;
+                const f32x4 er = *reinterpret_cast<const f32x4 *>(gE + 16 * tt + 4 * lg);
+                const f32x4 pd = *reinterpret_cast<const f32x4 *>(gPd + 16 * tt + 4 * lg);
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+                for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                    for (int kb = 0; kb < KBK; ++kb) {
-                        const Frag qf = frag_rows(Qs, L::LDK, 16 * tt, kb, lane);
-                        o = mma(o, qf, sh[kb][ct]);
-                        if constexpr (P::kBF16) o = mma(o, qf, sl[kb][ct]);
-                    }
+                    for (int i = 0; i < 4; ++i) QS[tt][ct][i] = er[i] * QS[tt][ct][i] + pd[i] * U[tt][ct][i];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int rr = 16 * tt + 4 * lg + i;
-                        o[i] = gE[rr] * o[i] + gPd[rr] * U[tt][ct][i];
-                    }
+                for (int kb = 0; kb < KBT; ++kb) {
+                    if (kb * P::KB < 16 * tt + 16) {
+                        const Frag ph = frag_rows(Ph, L::LDP, 16 * tt, kb, lane);
 #pragma unroll
-                    for (int kb = 0; kb < KBT; ++kb)
-                        if (kb <= kmax) {
-                            const Frag ph = frag_rows(Ph, L::LDT, 16 * tt, kb, lane);
-                            o = mma(o, ph, uh[kb][ct]);
-                            if constexpr (P::kBF16) {
-                                o = mma(o, ph, ul[kb][ct]);
-                                o = mma(o, frag_rows(Pl, L::LDT, 16 * tt, kb, lane), uh[kb][ct]);
-                            }
+                        for (int ct = 0; ct < CT; ++ct) {
+                            QS[tt][ct] = mma(QS[tt][ct], ph, uh[kb][ct]);
+                            if constexpr (P::kBF16) QS[tt][ct] = mma(QS[tt][ct], ph, ul[kb][ct]);
                         }
-                    // stage (scaled) for a row-contiguous store
+                        if constexpr (P::kBF16) {
+                            const Frag pl = frag_rows(Pl, L::LDP, 16 * tt, kb, lane);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int rr = 16 * tt + 4 * lg + i;
-                        const int cc = wave * WC + 16 * ct + lr;
-                        if (a.o_f32) Osf[rr * (W + 4) + cc] = a.scale * o[i];
-                        else st_op(Os + rr * L::LDV + cc, a.scale * o[i]);
+                            for (int ct = 0; ct < CT; ++ct) QS[tt][ct] = mma(QS[tt][ct], pl, uh[kb][ct]);
+                        }
                     }
                 }
             }
         }
-        // S <- e_last S + K^T diag(G_last) U
-        Frag dh[KBT][CT], dl[KBT][CT];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) U[tt][ct][i] *= gL[16 * tt + 4 * lg + i];
-#pragma unroll
-        for (int kb = 0; kb < KBT; ++kb)
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                if constexpr (P::kBF16) bfrag_split(U[2 * kb][ct], U[2 * kb + 1][ct], dh[kb][ct], dl[kb][ct]);
-                else dh[kb][ct] = U[kb][ct];
-            }
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                f32x4 s = S[rt][ct] * gam_c;
-#pragma unroll
-                for (int kb = 0; kb < KBT; ++kb) {
-                    if constexpr (P::kBF16) {
-                        const Frag kf = frag_rows(Kt, L::LDT, 16 * rt, kb, lane);
-                        s = mma(s, kf, dh[kb][ct]);
-                        s = mma(s, kf, dl[kb][ct]);
-                    } else {
-                        s = mma(s, frag_cols(reinterpret_cast<const float *>(Ks), L::LDK, 16 * rt, kb, lane),
-                                dh[kb][ct]);
-                    }
-                }
-                S[rt][ct] = s;
-            }
+        sync_lds();   // every wave is done with Q, T and P of this chunk
 
+        // ================= O staging (row-contiguous store) and K^T for the S update
+        const int64_t obase = replay ? orow0 + c0 : t0;
         if constexpr (WITH_O) {
             if (a.o_out) {
-                __syncthreads();
-                // row-contiguous store of the staged outputs (rows < len)
-                const int64_t obase = replay ? orow0 + c0 : t0;
                 if (a.o_f32) {
-                    constexpr int NV4 = W / 4;
                     float *og = reinterpret_cast<float *>(a.o_out);
-                    for (int e = tid; e < CH * NV4; e += NTHR) {
-                        const int rr = e / NV4, vc = e % NV4;
-                        if (rr < len)
-                            *reinterpret_cast<f32x4 *>(og + ((obase + rr) * a.h_v + h) * DV + cb * W + 4 * vc) =
-                                *reinterpret_cast<const f32x4 *>(Osf + rr * (W + 4) + 4 * vc);
-                    }
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int rr = 16 * tt + 4 * lg + i;
+                            if (rr < len) {
+#pragma unroll
+                                for (int ct = 0; ct < CT; ++ct)
+                                    og[((obase + rr) * a.h_v + h) * DV + col0 + 16 * ct + lr] = a.scale * QS[tt][ct][i];
+                            }
+                        }
                 } else {
-                    E *og = reinterpret_cast<E *>(a.o_out);
-                    for (int e = tid; e < CH * NVV; e += NTHR) {
-                        const int rr = e / NVV, vc = e % NVV;
-                        if (rr < len)
-                            *reinterpret_cast<u32x4 *>(og + ((obase + rr) * a.h_v + h) * DV + cb * W + VEC * vc) =
-                                *reinterpret_cast<const u32x4 *>(Os + rr * L::LDV + VEC * vc);
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int ct = 0; ct < CT; ++ct)
+                                st_op(Os + (16 * tt + 4 * lg + i) * L::LDO + wave * WC + 16 * ct + lr,
+                                      a.scale * QS[tt][ct][i]);
+                }
+            }
+        }
+        if constexpr (P::kBF16) {
+            // K^T[dk][t] as packed token pairs: thread -> (token pair, 8-column block)
+            constexpr int NCB8 = DK / 8;
+            static_assert((32 * NCB8) % NTHR == 0 || NTHR % (32 * NCB8) == 0, "K^T map");
+#pragma unroll
+            for (int j = 0; j < (32 * NCB8 + NTHR - 1) / NTHR; ++j) {
+                const int u = tid + j * NTHR;
+                if (u >= 32 * NCB8) break;
+                const int pr = u & 31, c8 = u >> 5;
+                const u32x4 x0 = *reinterpret_cast<const u32x4 *>(Ks + (2 * pr) * L::LDK + 8 * c8);
+                const u32x4 x1 = *reinterpret_cast<const u32x4 *>(Ks + (2 * pr + 1) * L::LDK + 8 * c8);
+                const uint32_t xs0[4] = {x0.x, x0.y, x0.z, x0.w}, xs1[4] = {x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = (xs0[e] & 0xffffu) | (xs1[e] << 16);
+                    const uint32_t hi = (xs0[e] >> 16) | (xs1[e] & 0xffff0000u);
+                    *reinterpret_cast<uint32_t *>(Kt + (8 * c8 + 2 * e) * L::LDKT + 2 * pr) = lo;
+                    *reinterpret_cast<uint32_t *>(Kt + (8 * c8 + 2 * e + 1) * L::LDKT + 2 * pr) = hi;
+                }
+            }
+        }
+        sync_lds();
+
+        // ================= S <- e_last S + K^T diag(G_last) U
+        {
+            Frag dh[KBT][CT], dl[KBT][CT];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const f32x4 lr4 = *reinterpret_cast<const f32x4 *>(gL + 16 * tt + 4 * lg);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) U[tt][ct][i] *= lr4[i];
+            }
+#pragma unroll
+            for (int kb = 0; kb < KBT; ++kb)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    if constexpr (P::kBF16) bfrag_split(U[2 * kb][ct], U[2 * kb + 1][ct], dh[kb][ct], dl[kb][ct]);
+                    else dh[kb][ct] = U[kb][ct];
+                }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    f32x4 s = S[rt][ct] * gam_c;
+#pragma unroll
+                    for (int kb = 0; kb < KBT; ++kb) {
+                        if constexpr (P::kBF16) {
+                            const Frag kf = frag_rows(Kt, L::LDKT, 16 * rt, kb, lane);
+                            s = mma(s, kf, dh[kb][ct]);
+                            s = mma(s, kf, dl[kb][ct]);
+                        } else {
+                            s = mma(s, frag_cols(reinterpret_cast<const float *>(Ks), L::LDK, 16 * rt, kb, lane),
+                                    dh[kb][ct]);
+                        }
                     }
+                    S[rt][ct] = s;
+                }
+                    }
+        }
+        // row-contiguous store of the staged outputs (rows < len)
+        if constexpr (WITH_O) {
+            if (a.o_out && !a.o_f32) {
+                E *og = reinterpret_cast<E *>(a.o_out);
+#pragma unroll
+                for (int j = 0; j < (CH * NVO + NTHR - 1) / NTHR; ++j) {
+                    const int e = tid + j * NTHR;
+                    const int rr = e / NVO, vc = e % NVO;
+                    if (e < CH * NVO && rr < len)
+                        *reinterpret_cast<u32x4 *>(og + ((obase + rr) * a.h_v + h) * DV + cb * W + VEC * vc) =
+                            *reinterpret_cast<const u32x4 *>(Os + rr * L::LDO + VEC * vc);
                 }
             }
         }
@@ -695,7 +801,7 @@ hipError_t launch_t(const ChunkArgs &a, hipStream_t stream)
     const int64_t nblk = (int64_t)a.n_seqs * a.h_v * (DV / W);
     if (nblk <= 0) return hipSuccess;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gdn_chunk_kernel<DK, DV, W, P, WITH_O>), dim3((unsigned)nblk), dim3(NTHR), 0,
+    hipLaunchKernelGGL((gdn_chunk_kernel<DK, DV, W, P, WITH_O>), dim3((unsigned)nblk), dim3(64 * (W / 16)), 0,
                        stream, a);
     return hipGetLastError();
 }
