@@ -150,19 +150,36 @@ __device__ __forceinline__ void st_op(uint16_t *p, float x) { *p = f2bf(x); }
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(uint16_t x) { return bf2f(x); }
 
-// A fragment of T_off, the strictly-lower part of T (stored in LDS as fp32 with zeros
-// on and above the diagonal), converted to the operand type of the policy.
+
+// A fragment read from a fp32 64-column LDS matrix (row stride LDF), converted to the
+// operand type of the policy.
 template <class P>
-__device__ __forceinline__ typename P::Frag tfrag(const float *Tf, int r0, int kb, int lane) {
+__device__ __forceinline__ typename P::Frag afrag_f32(const float *M, int r0, int kb, int lane) {
     const int row = r0 + (lane & 15);
     if constexpr (P::kBF16) {
         const int k0 = kb * 32 + 4 * (lane >> 4);
-        const f32x4 x = *reinterpret_cast<const f32x4 *>(Tf + row * LDF + k0);
-        const f32x4 y = *reinterpret_cast<const f32x4 *>(Tf + row * LDF + k0 + 16);
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(M + row * LDF + k0);
+        const f32x4 y = *reinterpret_cast<const f32x4 *>(M + row * LDF + k0 + 16);
         const u32x4 u = {pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(y[0], y[1]), pack2(y[2], y[3])};
         return __builtin_bit_cast(bf16x8, u);
     } else {
-        return *reinterpret_cast<const f32x4 *>(Tf + row * LDF + kb * 16 + 4 * (lane >> 4));
+        return *reinterpret_cast<const f32x4 *>(M + row * LDF + kb * 16 + 4 * (lane >> 4));
+    }
+}
+
+// Row-contiguous store of a staged chunk of outputs (rows < len) for one v-head.
+template <class E, int DV, int W, int NVO, int NTHR, int LDO>
+__device__ __forceinline__ void store_o(const ChunkArgs &a, const E *Os, int64_t obase, int len,
+                                        int h, int cb, int tid) {
+    constexpr int VEC = 16 / (int)sizeof(E);
+    E *og = reinterpret_cast<E *>(a.o_out);
+#pragma unroll
+    for (int j = 0; j < (CH * NVO) / NTHR; ++j) {
+        const int e = tid + j * NTHR;
+        const int rr = e / NVO, vc = e % NVO;
+        if (rr < len)
+            *reinterpret_cast<u32x4 *>(og + ((obase + rr) * a.h_v + h) * DV + cb * W + VEC * vc) =
+                *reinterpret_cast<const u32x4 *>(Os + rr * LDO + VEC * vc);
     }
 }
 
@@ -191,6 +208,47 @@ __device__ __forceinline__ float v_at(const typename VHold<P>::T *v, int i) {
     else return v[i];
 }
 
+
+// One lower-triangular 16x16 tile (ti, tj) of a chunk Gram product and its use:
+//   K K^T tile -> -A = -b_r G_rc (K K^T)_rc  (fp32, c < r)
+//   Q K^T tile ->  P = G_rc (Q K^T)_rc (c < r) and its diagonal (Q K^T)_rr
+// with G_rc = exp(H_r - H_c) when no alpha = 0 token lies in (c, r].
+template <class P, int KBK, int LDK, int LDP>
+__device__ __forceinline__ void gram_tile(bool isP, int ti, int tj, const typename P::E *Ks,
+                                          const typename P::E *Qs, float *nA, typename P::E *Ph,
+                                          typename P::E *Pl, const float *gH, const float *gB,
+                                          const int *gR, float *gPd, int lane) {
+    const int lr = lane & 15, lg = lane >> 4;
+    f32x4 gr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KBK; ++kb)
+        gr = mma(gr, frag_rows(isP ? Qs : Ks, LDK, 16 * ti, kb, lane), frag_rows(Ks, LDK, 16 * tj, kb, lane));
+    const int c = 16 * tj + lr;
+    const float hc = gH[c];
+    const f32x4 hr = *reinterpret_cast<const f32x4 *>(gH + 16 * ti + 4 * lg);
+    const f32x4 br = *reinterpret_cast<const f32x4 *>(gB + 16 * ti + 4 * lg);
+    const int4 rr4 = *reinterpret_cast<const int4 *>(gR + 16 * ti + 4 * lg);
+    const int rrs[4] = {rr4.x, rr4.y, rr4.z, rr4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rr = 16 * ti + 4 * lg + i;
+        const float gam = (c < rr && rrs[i] <= c) ? __expf(hr[i] - hc) : 0.f;
+        if (!isP) {
+            nA[rr * LDF + c] = -br[i] * gam * gr[i];
+        } else {
+            const float pv = gam * gr[i];
+            if constexpr (P::kBF16) {
+                const uint16_t hb = f2bf(pv);
+                Ph[rr * LDP + c] = hb;
+                Pl[rr * LDP + c] = f2bf(pv - bf2f(hb));
+            } else {
+                Ph[rr * LDP + c] = pv;
+            }
+            if (c == rr) gPd[rr] = gr[i];
+        }
+    }
+}
+
 // Workgroup barrier that orders LDS only: global loads stay in flight across it
 // (a full __syncthreads also waits for every outstanding global load).
 __device__ __forceinline__ void sync_lds() {
@@ -207,12 +265,11 @@ __device__ __forceinline__ void tri_tile(int idx, int &ti, int &tj) {
 }
 
 // ---------------------------------------------------------------- LDS plan
-// Four regions, reused across the phases of one chunk so that a workgroup needs
-// at most ~75 KB and two workgroups share a CU:
-//   K   K chunk, row-major                      (Gram, X = K S, source of K^T)
-//   Q   Q chunk, row-major; then O staging      (Gram, Q S; row-contiguous o store)
-//   T   T = (I + A)^{-1} fp32; then K^T (bf16)  (inversion, U = T Y; S update)
-//   P   A fp32 + inversion scratch; then P      (inversion; P U)
+// One workgroup per CU; every region has a single role within a chunk:
+//   G  gate arrays (first, so their offsets fit the DS immediate)
+//   K  K chunk, row-major         Q  Q chunk, row-major       Kt  K^T (bf16 only)
+//   A  -A (fp32)                  T  block-diagonal inverses T_bb - I (fp32)
+//   P  P = strict_lower(Q K^T o G) (bf16 hi + lo, or fp32)    O  output staging
 template <int DK, int DV, int W, class P>
 struct Lds {
     typedef typename P::E E;
@@ -220,22 +277,15 @@ struct Lds {
     static constexpr int LDO = W + P::PAD;           // O staging rows
     static constexpr int LDKT = CH + 4;              // K^T rows (bf16)
     static constexpr int LDP = CH + P::PAD;          // P rows
-    static constexpr int nK = CH * LDK * (int)sizeof(E);
-    static constexpr int nQ0 = CH * LDK * (int)sizeof(E);
-    static constexpr int nO = CH * LDO * (int)sizeof(E);
-    static constexpr int nQ = nQ0 > nO ? nQ0 : nO;
-    static constexpr int nT0 = CH * LDF * 4;
-    static constexpr int nKt = P::kBF16 ? DK * LDKT * 2 : 0;
-    static constexpr int nT = nT0 > nKt ? nT0 : nKt;
-    static constexpr int nA = CH * LDF * 4 + 4 * 16 * LDX * 4;          // A + 4 scratch tiles
-    static constexpr int nPP = (P::kBF16 ? 2 : 1) * CH * LDP * (int)sizeof(E);
-    static constexpr int nP = nA > nPP ? nA : nPP;
-    static constexpr int oG = 0;                     // gate arrays first: small offsets
+    static constexpr int oG = 0;
     static constexpr int oK = 6 * CH * 4 + 64;
-    static constexpr int oQ = oK + nK;
-    static constexpr int oT = oQ + nQ;
-    static constexpr int oP = oT + nT;
-    static constexpr int bytes = oP + nP;
+    static constexpr int oQ = oK + CH * LDK * (int)sizeof(E);
+    static constexpr int oKt = oQ + CH * LDK * (int)sizeof(E);
+    static constexpr int oA = oKt + (P::kBF16 ? DK * LDKT * 2 : 0);
+    static constexpr int oT = oA + CH * LDF * 4;
+    static constexpr int oP = oT + CH * LDF * 4;
+    static constexpr int oO = oP + (P::kBF16 ? 2 : 1) * CH * LDP * (int)sizeof(E);
+    static constexpr int bytes = oO + CH * LDO * (int)sizeof(E);
 };
 
 // ---------------------------------------------------------------- kernel
@@ -247,25 +297,21 @@ __global__ void __launch_bounds__(64 * (W / 16)) gdn_chunk_kernel(ChunkArgs a)
     typedef typename P::E E;
     typedef typename P::Frag Frag;
     typedef Lds<DK, DV, W, P> L;
-    constexpr int WC = W / NWAVE;          // columns per wave
-    constexpr int CT = WC / 16;            // column tiles per wave
     constexpr int RT = DK / 16;            // row tiles of S
     constexpr int KBK = DK / P::KB;        // k-blocks over d_k
     constexpr int KBT = CH / P::KB;        // k-blocks over the chunk's tokens
     constexpr int NCB = DV / W;            // column blocks per head
-    static_assert(CT >= 1 && WC % 16 == 0, "wave column slab must be a multiple of 16");
-    static_assert(L::bytes <= 96 * 1024, "LDS plan");
+    static_assert(L::bytes <= 160 * 1024, "LDS plan");
 
     __shared__ __attribute__((aligned(16))) char smem[L::bytes];
     E *Ks = reinterpret_cast<E *>(smem + L::oK);
     E *Qs = reinterpret_cast<E *>(smem + L::oQ);
-    E *Os = reinterpret_cast<E *>(smem + L::oQ);
-    float *Tf = reinterpret_cast<float *>(smem + L::oT);
-    uint16_t *Kt = reinterpret_cast<uint16_t *>(smem + L::oT);
-    float *Af = reinterpret_cast<float *>(smem + L::oP);
-    float *Xs = Af + CH * LDF;
+    uint16_t *Kt = reinterpret_cast<uint16_t *>(smem + L::oKt);
+    float *nA = reinterpret_cast<float *>(smem + L::oA);
+    float *Tb = reinterpret_cast<float *>(smem + L::oT);
     E *Ph = reinterpret_cast<E *>(smem + L::oP);
     E *Pl = Ph + CH * L::LDP;
+    E *Os = reinterpret_cast<E *>(smem + L::oO);
     float *gH = reinterpret_cast<float *>(smem + L::oG);   // cumulative log-gate since last reset
     float *gE = gH + CH;       // e_i
     float *gB = gE + CH;       // beta_i
@@ -275,7 +321,6 @@ __global__ void __launch_bounds__(64 * (W / 16)) gdn_chunk_kernel(ChunkArgs a)
     int64_t *gMisc = reinterpret_cast<int64_t *>(gR + CH);
 
     const int tid0 = threadIdx.x, wave = tid0 >> 6;
-
     int tid = tid0, lane = tid0 & 63, lr = lane & 15, lg = lane >> 4;
 
     // ---- block -> (sequence, v-head, column block); XCD-aware: consecutive logical
@@ -323,6 +368,9 @@ __global__ void __launch_bounds__(64 * (W / 16)) gdn_chunk_kernel(ChunkArgs a)
         }
         if (lane == 0) gMisc[0] = row0;
     }
+    // T_bb regions outside the diagonal blocks are read (and multiplied by zeros):
+    // keep them finite
+    for (int e = tid; e < CH * LDF; e += NTHR) Tb[e] = 0.f;
     __syncthreads();
     const int64_t orow0 = gMisc[0];
     if (orow0 < 0 || orow0 + rn > (replay ? a.total_out : a.total_tokens)) return;
@@ -331,23 +379,21 @@ __global__ void __launch_bounds__(64 * (W / 16)) gdn_chunk_kernel(ChunkArgs a)
         if (n == a.n_seqs - 1) a.cu_out[n + 1] = (int32_t)(orow0 + rn);
     }
 
-    const int col0 = cb * W + wave * WC;       // first d_v column of this wave
+    const int col0 = cb * W + wave * 16;       // first d_v column of this wave
     const int64_t sbase = ((int64_t)n * a.h_v + h) * DK * DV;
 
-    // ---- state: S[rt][ct] holds rows 16rt.., columns col0 + 16ct..
-    f32x4 S[RT][CT];
+    // ---- state: S[rt] holds rows 16rt.. of columns col0..col0+15
+    f32x4 S[RT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt) {
+        if (!replay && a.S0) {
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            if (!replay && a.S0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    S[rt][ct][i] = a.S0[sbase + (int64_t)(16 * rt + 4 * lg + i) * DV + col0 + 16 * ct + lr];
-            } else {
-                S[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+            for (int i = 0; i < 4; ++i)
+                S[rt][i] = a.S0[sbase + (int64_t)(16 * rt + 4 * lg + i) * DV + col0 + lr];
+        } else {
+            S[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+    }
 
     const E *qg = reinterpret_cast<const E *>(a.q);
     const E *kg = reinterpret_cast<const E *>(a.k);
@@ -355,14 +401,14 @@ __global__ void __launch_bounds__(64 * (W / 16)) gdn_chunk_kernel(ChunkArgs a)
     constexpr int VEC = 16 / (int)sizeof(E);   // elements per 16-byte vector
     constexpr int NVK = DK / VEC;              // vectors per K/Q row
     constexpr int NVO = W / VEC;               // vectors per O row (this column block)
-    static_assert(NVK <= 64 && (64 % NVK) == 0 && (256 % NVO) == 0, "vector map");
+    static_assert(NVK <= 64 && (64 % NVK) == 0 && (CH * NVO) % NTHR == 0, "vector maps");
 
     constexpr int RPP = NTHR / NVK;            // K/Q rows per pass of the workgroup
     constexpr int NPF = CH / RPP;              // passes per chunk
     u32x4 kpf[NPF], qpf[NPF];
     float gpf = 0.f, bpf = 0.f;
     bool gok = false;
-    typename VHold<P>::T vnext[4][CT][VHold<P>::N];
+    typename VHold<P>::T vnext[4][VHold<P>::N];
     auto fetch = [&](int64_t cc) {
         const int ln = (int)((rn - cc) < CH ? (rn - cc) : CH);
         const int64_t tb = wbeg + cc;
@@ -383,12 +429,12 @@ __global__ void __launch_bounds__(64 * (W / 16)) gdn_chunk_kernel(ChunkArgs a)
         }
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-                load_v_rows<P>(vnext[tt][ct], vg, tb, 16 * tt + 4 * lg, ln, a.h_v, h, DV, col0 + 16 * ct + lr);
+            load_v_rows<P>(vnext[tt], vg, tb, 16 * tt + 4 * lg, ln, a.h_v, h, DV, col0 + lr);
     };
     if (rn > 0) fetch(0);
 
+    int64_t opend = -1;        // first output row of the chunk staged in Os, if any
+    int olen = 0;
     for (int64_t c0 = 0; c0 < rn; c0 += CH) {
         const int len = (int)((rn - c0) < CH ? (rn - c0) : CH);
         const int64_t t0 = wbeg + c0;
@@ -399,9 +445,13 @@ __global__ void __launch_bounds__(64 * (W / 16)) gdn_chunk_kernel(ChunkArgs a)
         const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
         sync_lds();
 
-        // ================= chunk inputs (prefetched during the previous chunk's state pass)
-        // into LDS.  Rows >= len repeat the last token's q/k/v but get g = 0 and beta = 0:
-        // a token with alpha = 1 and no write leaves S unchanged, and its pseudo-value is 0
+        // ================= P0: store the previous chunk's staged outputs; this chunk's
+        // K, Q into LDS (prefetched during the previous chunk); gate scan.
+        // Rows >= len repeat the last token's q/k/v but get g = 0 and beta = 0: a token
+        // with alpha = 1 and no write leaves S unchanged, and its pseudo-value is 0.
+        if constexpr (WITH_O) {
+            if (opend >= 0) store_o<E, DV, W, NVO, NTHR, L::LDO>(a, Os, opend, olen, h, cb, tid);
+        }
 #pragma unroll
         for (int p = 0; p < NPF; ++p) {
             const int row = p * RPP + tid / NVK;
@@ -436,34 +486,50 @@ __global__ void __launch_bounds__(64 * (W / 16)) gdn_chunk_kernel(ChunkArgs a)
         }
         sync_lds();
 
-        // ================= A = strict_lower(diag(b) (K K^T o G))
-        // G_rc = exp(H_r - H_c) when no reset in (c, r]
+        // ================= P1: X = K S and Q S (S as hi, hi + lo); the K K^T Gram tiles
+        // forming -A = -strict_lower(diag(b) (K K^T o G)).
+        f32x4 X[4], QS[4];
 #pragma unroll
-        for (int j = 0; j < (10 + NWAVE - 1) / NWAVE; ++j) {
-            const int idx = wave + NWAVE * j;
-            if (idx < 10) {
-                int ti, tj;
-                tri_tile(idx, ti, tj);
-                f32x4 gr = {0.f, 0.f, 0.f, 0.f};
+        for (int tt = 0; tt < 4; ++tt) {
+            X[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            QS[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-                for (int kb = 0; kb < KBK; ++kb)
-                    gr = mma(gr, frag_rows(Ks, L::LDK, 16 * ti, kb, lane), frag_rows(Ks, L::LDK, 16 * tj, kb, lane));
-                const int c = 16 * tj + lr;
-                const float hc = gH[c];
-                const f32x4 hr = *reinterpret_cast<const f32x4 *>(gH + 16 * ti + 4 * lg);
-                const f32x4 br = *reinterpret_cast<const f32x4 *>(gB + 16 * ti + 4 * lg);
+        for (int kb = 0; kb < KBK; ++kb) {
+            Frag sh, sl;
+            if constexpr (P::kBF16) bfrag_split(S[2 * kb], S[2 * kb + 1], sh, sl);
+            else sh = S[kb];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rr = 16 * ti + 4 * lg + i;
-                    const float gam = (c < rr && gR[rr] <= c) ? __expf(hr[i] - hc) : 0.f;
-                    Af[rr * LDF + c] = br[i] * gam * gr[i];
+            for (int tt = 0; tt < 4; ++tt) {
+                X[tt] = mma(X[tt], frag_rows(Ks, L::LDK, 16 * tt, kb, lane), sh);
+                if constexpr (WITH_O) {
+                    const Frag qf = frag_rows(Qs, L::LDK, 16 * tt, kb, lane);
+                    QS[tt] = mma(QS[tt], qf, sh);
+                    if constexpr (P::kBF16) QS[tt] = mma(QS[tt], qf, sl);
                 }
             }
+        }
+        {
+            // the 10 K K^T tiles over the waves (two per wave when there are 4 waves)
+            static_assert(NWAVE == 4 || NWAVE == 8, "tile schedule");
+            int ti, tj;
+            tri_tile(wave, ti, tj);
+            gram_tile<P, KBK, L::LDK, L::LDP>(false, ti, tj, Ks, Qs, nA, Ph, Pl, gH, gB, gR, gPd, lane);
+            if (wave + NWAVE < 10) {
+                tri_tile(wave + NWAVE, ti, tj);
+                gram_tile<P, KBK, L::LDK, L::LDP>(false, ti, tj, Ks, Qs, nA, Ph, Pl, gH, gB, gR, gPd, lane);
             }
+            if (NWAVE == 4 && wave < 2) {
+                tri_tile(wave + 8, ti, tj);
+                gram_tile<P, KBK, L::LDK, L::LDP>(false, ti, tj, Ks, Qs, nA, Ph, Pl, gH, gB, gR, gPd, lane);
+            }
+        }
         sync_lds();
 
-        // ================= T = (I + A)^{-1} in fp32 (blocked, 16x16 diagonal blocks)
-        // level 0: wave b inverts diagonal block b by forward substitution (column = lane)
+        // ================= P2: diagonal-block inverses T_bb = (I + A_bb)^{-1} by forward
+        // substitution (first half of the waves, one column per lane), stored as T_bb - I;
+        // P = strict_lower(Q K^T o G) and K^T (second half); Y = b (V - e X) (every wave);
+        // then the next chunk's inputs are fetched.
         if (wave < 4 && lane < 16) {
             const int b0 = 16 * wave;
             const int c = lane;
@@ -472,216 +538,122 @@ __global__ void __launch_bounds__(64 * (W / 16)) gdn_chunk_kernel(ChunkArgs a)
             for (int i = 0; i < 16; ++i) {
                 float s = 0.f;
 #pragma unroll
-                for (int j = 0; j < i; ++j) s = fmaf(Af[(b0 + i) * LDF + b0 + j], t[j], s);
-                t[i] = i < c ? 0.f : (i == c ? 1.f : -s);
+                for (int j = 0; j < i; ++j) s = fmaf(nA[(b0 + i) * LDF + b0 + j], t[j], s);
+                t[i] = i < c ? 0.f : (i == c ? 1.f : s);
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) Tb[(b0 + i) * LDF + b0 + c] = i == c ? 0.f : t[i];
+        }
+        if (wave >= NWAVE / 2) {
+            // the other half of the waves: the 10 Q K^T tiles (P) and K^T, while the
+            // first half inverts the diagonal blocks
+            const int w2 = wave - NWAVE / 2;            // 0..NWAVE/2-1
+            if constexpr (WITH_O) {
+#pragma unroll
+                for (int j = 0; j < (10 + NWAVE / 2 - 1) / (NWAVE / 2); ++j) {
+                    const int idx = w2 + (NWAVE / 2) * j;
+                    if (idx < 10) {
+                        int ti, tj;
+                        tri_tile(idx, ti, tj);
+                        gram_tile<P, KBK, L::LDK, L::LDP>(true, ti, tj, Ks, Qs, nA, Ph, Pl, gH, gB, gR, gPd, lane);
                     }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) Tf[(b0 + i) * LDF + b0 + c] = t[i];
-        }
-        sync_lds();
-        // level 1: T_{b+1,b} = -T_{b+1,b+1} A_{b+1,b} T_{b,b} for b = 0 (wave 0), 2 (wave 1)
-        if (wave < 2) {
-            const int b = 2 * wave;
-            f32x4 x = {0.f, 0.f, 0.f, 0.f};
-            x = mma(x, frag_rows(Af, LDF, 16 * (b + 1), b, lane), frag_cols(Tf, LDF, 16 * b, b, lane));
-            f32x4 y = {0.f, 0.f, 0.f, 0.f};
-            y = mma(y, frag_rows(Tf, LDF, 16 * (b + 1), b + 1, lane), x);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Tf[(16 * (b + 1) + 4 * lg + i) * LDF + 16 * b + lr] = -y[i];
-        }
-        sync_lds();
-        // level 2: lower-left 32x32 block = -T_lowerright A_21 T_upperleft
-        if (wave < 4) {
-            const int la = wave >> 1, lb = wave & 1;
-            f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-                if (c >= lb)
-                    x = mma(x, frag_rows(Af, LDF, 16 * (2 + la), c, lane),
-                            frag_cols(Tf, LDF, 16 * lb, c, lane));
-            float *X = Xs + (la * 2 + lb) * 16 * LDX;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) X[(4 * lg + i) * LDX + lr] = x[i];
-        }
-        sync_lds();
-        if (wave < 4) {
-            const int la = wave >> 1, lb = wave & 1;
-            f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int d = 0; d < 2; ++d)
-                if (d <= la)
-                    y = mma(y, frag_rows(Tf, LDF, 16 * (2 + la), 2 + d, lane),
-                            frag_cols(Xs + (d * 2 + lb) * 16 * LDX, LDX, 0, 0, lane));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Tf[(16 * (2 + la) + 4 * lg + i) * LDF + 16 * lb + lr] = -y[i];
-        }
-        // T_off keeps only the strictly-lower part: clear the diagonal and above
-        // (entries no wave writes in this phase)
-#pragma unroll
-        for (int j = 0; j < CH * CH / NTHR; ++j) {
-            const int e = tid + j * NTHR;
-            const int rr = e >> 6, c = e & 63;
-            if (c >= rr) Tf[rr * LDF + c] = 0.f;
-        }
-        sync_lds();
-
-        // ================= P = strict_lower(Q K^T o G) and its diagonal (Q K^T)_ii
-        if constexpr (WITH_O) {
-#pragma unroll
-            for (int j = 0; j < (10 + NWAVE - 1) / NWAVE; ++j) {
-                const int idx = wave + NWAVE * j;
-                if (idx < 10) {
-                    int ti, tj;
-                    tri_tile(idx, ti, tj);
-                    f32x4 gr = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kb = 0; kb < KBK; ++kb)
-                        gr = mma(gr, frag_rows(Qs, L::LDK, 16 * ti, kb, lane), frag_rows(Ks, L::LDK, 16 * tj, kb, lane));
-                    const int c = 16 * tj + lr;
-                    const float hc = gH[c];
-                    const f32x4 hr = *reinterpret_cast<const f32x4 *>(gH + 16 * ti + 4 * lg);
+                }
+                if (P::kBF16 && w2 < 2) {
+                    // zero the upper tiles (0,1) and (2,3) that 32-wide k-blocks of P read
+                    const int ti = 2 * w2, tj = ti + 1;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int rr = 16 * ti + 4 * lg + i;
-                        const float pv = (c < rr && gR[rr] <= c) ? __expf(hr[i] - hc) * gr[i] : 0.f;
-                        if constexpr (P::kBF16) {
-                            const uint16_t hb = f2bf(pv);
-                            Ph[rr * L::LDP + c] = hb;
-                            Pl[rr * L::LDP + c] = f2bf(pv - bf2f(hb));
-                        } else {
-                            Ph[rr * L::LDP + c] = pv;
+                        const int rr = 16 * ti + 4 * lg + i, c = 16 * tj + lr;
+                        Ph[rr * L::LDP + c] = 0;
+                        Pl[rr * L::LDP + c] = 0;
+                    }
+                }
+            }
+            if constexpr (P::kBF16) {
+                // K^T[dk][t] as packed token pairs: thread -> (token pair, 8-column block)
+                constexpr int NCB8 = DK / 8;
+                static_assert((32 * NCB8) % (NTHR / 2) == 0 || (NTHR / 2) % (32 * NCB8) == 0, "K^T map");
+#pragma unroll
+                for (int j = 0; j < (32 * NCB8 + NTHR / 2 - 1) / (NTHR / 2); ++j) {
+                    const int u = (tid - NTHR / 2) + j * (NTHR / 2);
+                    if (u < 32 * NCB8) {
+                        const int pr = u & 31, c8 = u >> 5;
+                        const u32x4 x0 = *reinterpret_cast<const u32x4 *>(Ks + (2 * pr) * L::LDK + 8 * c8);
+                        const u32x4 x1 = *reinterpret_cast<const u32x4 *>(Ks + (2 * pr + 1) * L::LDK + 8 * c8);
+                        const uint32_t xs0[4] = {x0.x, x0.y, x0.z, x0.w}, xs1[4] = {x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t lo = (xs0[e] & 0xffffu) | (xs1[e] << 16);
+                            const uint32_t hi = (xs0[e] >> 16) | (xs1[e] & 0xffff0000u);
+                            *reinterpret_cast<uint32_t *>(Kt + (8 * c8 + 2 * e) * L::LDKT + 2 * pr) = lo;
+                            *reinterpret_cast<uint32_t *>(Kt + (8 * c8 + 2 * e + 1) * L::LDKT + 2 * pr) = hi;
                         }
-                        if (c == rr) gPd[rr] = gr[i];
                     }
-                }
-                    }
-            if (P::kBF16 && wave < 2) {
-                // zero the upper tiles (0,1) and (2,3) that 32-wide k-blocks of P read
-                const int ti = 2 * wave, tj = ti + 1;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rr = 16 * ti + 4 * lg + i, c = 16 * tj + lr;
-                    Ph[rr * L::LDP + c] = 0;
-                    Pl[rr * L::LDP + c] = 0;
                 }
             }
-            sync_lds();
         }
-
-        // ================= state pass on this wave's columns
-        const float gam_c = gE[CH - 1];
-        // X = K S (S as hi bf16) and Q S (S as hi + lo), k-block by k-block
-        f32x4 X[4][CT], QS[4][CT];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                X[tt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-                QS[tt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-        for (int kb = 0; kb < KBK; ++kb) {
-            Frag sh[CT], sl[CT];
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                if constexpr (P::kBF16) bfrag_split(S[2 * kb][ct], S[2 * kb + 1][ct], sh[ct], sl[ct]);
-                else sh[ct] = S[kb][ct];
-            }
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                const Frag kf = frag_rows(Ks, L::LDK, 16 * tt, kb, lane);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) X[tt][ct] = mma(X[tt][ct], kf, sh[ct]);
-                if constexpr (WITH_O) {
-                    const Frag qf = frag_rows(Qs, L::LDK, 16 * tt, kb, lane);
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) {
-                        QS[tt][ct] = mma(QS[tt][ct], qf, sh[ct]);
-                        if constexpr (P::kBF16) QS[tt][ct] = mma(QS[tt][ct], qf, sl[ct]);
-                    }
-                }
-            }
-            }
-        // Y = b (V - e X), in place
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             const f32x4 br = *reinterpret_cast<const f32x4 *>(gB + 16 * tt + 4 * lg);
             const f32x4 er = *reinterpret_cast<const f32x4 *>(gE + 16 * tt + 4 * lg);
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    X[tt][ct][i] = br[i] * (v_at<P>(vnext[tt][ct], i) - er[i] * X[tt][ct][i]);
+            for (int i = 0; i < 4; ++i) X[tt][i] = br[i] * (v_at<P>(vnext[tt], i) - er[i] * X[tt][i]);
         }
-        // every input of this chunk is consumed: fetch the next chunk's, which land while
-        // the rest of this chunk is processed
+        // every input of this chunk is consumed: the next chunk's land while the rest of
+        // this chunk is processed
         if (c0 + CH < rn) fetch(c0 + CH);
-        // U = Y + T_off Y  (unit diagonal exact; T_off read from the fp32 inverse)
-        f32x4 U[4][CT];
-        {
-            Frag yf[KBT][CT];
+        sync_lds();
+
+        // ================= P3: (I + A) U = Y by 16-row block forward substitution
+        //   U_b = Z_b + (T_bb - I) Z_b,   Z_b = Y_b - sum_{j<b} A_bj U_j
+        // (unit diagonal exact in fp32); then O and the state update.
+        f32x4 U[4];
 #pragma unroll
-            for (int kb = 0; kb < KBT; ++kb)
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    if constexpr (P::kBF16) yf[kb][ct] = bfrag_hi(X[2 * kb][ct], X[2 * kb + 1][ct]);
-                    else yf[kb][ct] = X[kb][ct];
+        for (int b = 0; b < 4; ++b) {
+            f32x4 z = X[b];
+            if constexpr (P::kBF16) {
+                if (b >= 1) {
+                    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                    z = mma(z, afrag_f32<P>(nA, 16 * b, 0, lane), bfrag_hi(U[0], b >= 2 ? U[1] : zero));
+                    if (b == 3) z = mma(z, afrag_f32<P>(nA, 16 * b, 1, lane), bfrag_hi(U[2], zero));
                 }
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                const Frag zf = (b & 1) ? bfrag_hi(zero, z) : bfrag_hi(z, zero);
+                U[b] = mma(z, afrag_f32<P>(Tb, 16 * b, b >> 1, lane), zf);
+            } else {
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) U[tt][ct] = X[tt][ct];
-#pragma unroll
-                for (int kb = 0; kb < KBT; ++kb) {
-                    if (kb * P::KB < 16 * tt + 16) {
-                        const Frag tf = tfrag<P>(Tf, 16 * tt, kb, lane);
-#pragma unroll
-                        for (int ct = 0; ct < CT; ++ct) U[tt][ct] = mma(U[tt][ct], tf, yf[kb][ct]);
-                    }
-                }
+                for (int j = 0; j < 4; ++j)
+                    if (j < b) z = mma(z, afrag_f32<P>(nA, 16 * b, j, lane), U[j]);
+                U[b] = mma(z, afrag_f32<P>(Tb, 16 * b, b, lane), z);
             }
         }
         // O = e (Q S) + Pd U + P_off U   (QS registers become O)
         if constexpr (WITH_O) {
-            Frag uh[KBT][CT], ul[KBT][CT];
+            Frag uh[KBT], ul[KBT];
 #pragma unroll
-            for (int kb = 0; kb < KBT; ++kb)
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    if constexpr (P::kBF16) bfrag_split(U[2 * kb][ct], U[2 * kb + 1][ct], uh[kb][ct], ul[kb][ct]);
-                    else uh[kb][ct] = U[kb][ct];
-                }
+            for (int kb = 0; kb < KBT; ++kb) {
+                if constexpr (P::kBF16) bfrag_split(U[2 * kb], U[2 * kb + 1], uh[kb], ul[kb]);
+                else uh[kb] = U[kb];
+            }
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 const f32x4 er = *reinterpret_cast<const f32x4 *>(gE + 16 * tt + 4 * lg);
                 const f32x4 pd = *reinterpret_cast<const f32x4 *>(gPd + 16 * tt + 4 * lg);
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) QS[tt][ct][i] = er[i] * QS[tt][ct][i] + pd[i] * U[tt][ct][i];
+                for (int i = 0; i < 4; ++i) QS[tt][i] = er[i] * QS[tt][i] + pd[i] * U[tt][i];
 #pragma unroll
                 for (int kb = 0; kb < KBT; ++kb) {
                     if (kb * P::KB < 16 * tt + 16) {
                         const Frag ph = frag_rows(Ph, L::LDP, 16 * tt, kb, lane);
-#pragma unroll
-                        for (int ct = 0; ct < CT; ++ct) {
-                            QS[tt][ct] = mma(QS[tt][ct], ph, uh[kb][ct]);
-                            if constexpr (P::kBF16) QS[tt][ct] = mma(QS[tt][ct], ph, ul[kb][ct]);
-                        }
+                        QS[tt] = mma(QS[tt], ph, uh[kb]);
                         if constexpr (P::kBF16) {
-                            const Frag pl = frag_rows(Pl, L::LDP, 16 * tt, kb, lane);
-#pragma unroll
-                            for (int ct = 0; ct < CT; ++ct) QS[tt][ct] = mma(QS[tt][ct], pl, uh[kb][ct]);
+                            QS[tt] = mma(QS[tt], ph, ul[kb]);
+                            QS[tt] = mma(QS[tt], frag_rows(Pl, L::LDP, 16 * tt, kb, lane), uh[kb]);
                         }
                     }
                 }
             }
-        }
-        sync_lds();   // every wave is done with Q, T and P of this chunk
-
-        // ================= O staging (row-contiguous store) and K^T for the S update
-        const int64_t obase = replay ? orow0 + c0 : t0;
-        if constexpr (WITH_O) {
+            const int64_t obase = replay ? orow0 + c0 : t0;
             if (a.o_out) {
                 if (a.o_f32) {
                     float *og = reinterpret_cast<float *>(a.o_out);
@@ -690,98 +662,55 @@ __global__ void __launch_bounds__(64 * (W / 16)) gdn_chunk_kernel(ChunkArgs a)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const int rr = 16 * tt + 4 * lg + i;
-                            if (rr < len) {
-#pragma unroll
-                                for (int ct = 0; ct < CT; ++ct)
-                                    og[((obase + rr) * a.h_v + h) * DV + col0 + 16 * ct + lr] = a.scale * QS[tt][ct][i];
-                            }
+                            if (rr < len) og[((obase + rr) * a.h_v + h) * DV + col0 + lr] = a.scale * QS[tt][i];
                         }
                 } else {
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
-#pragma unroll
-                            for (int ct = 0; ct < CT; ++ct)
-                                st_op(Os + (16 * tt + 4 * lg + i) * L::LDO + wave * WC + 16 * ct + lr,
-                                      a.scale * QS[tt][ct][i]);
+                            st_op(Os + (16 * tt + 4 * lg + i) * L::LDO + wave * 16 + lr, a.scale * QS[tt][i]);
+                    opend = obase;
+                    olen = len;
                 }
             }
         }
-        if constexpr (P::kBF16) {
-            // K^T[dk][t] as packed token pairs: thread -> (token pair, 8-column block)
-            constexpr int NCB8 = DK / 8;
-            static_assert((32 * NCB8) % NTHR == 0 || NTHR % (32 * NCB8) == 0, "K^T map");
-#pragma unroll
-            for (int j = 0; j < (32 * NCB8 + NTHR - 1) / NTHR; ++j) {
-                const int u = tid + j * NTHR;
-                if (u >= 32 * NCB8) break;
-                const int pr = u & 31, c8 = u >> 5;
-                const u32x4 x0 = *reinterpret_cast<const u32x4 *>(Ks + (2 * pr) * L::LDK + 8 * c8);
-                const u32x4 x1 = *reinterpret_cast<const u32x4 *>(Ks + (2 * pr + 1) * L::LDK + 8 * c8);
-                const uint32_t xs0[4] = {x0.x, x0.y, x0.z, x0.w}, xs1[4] = {x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t lo = (xs0[e] & 0xffffu) | (xs1[e] << 16);
-                    const uint32_t hi = (xs0[e] >> 16) | (xs1[e] & 0xffff0000u);
-                    *reinterpret_cast<uint32_t *>(Kt + (8 * c8 + 2 * e) * L::LDKT + 2 * pr) = lo;
-                    *reinterpret_cast<uint32_t *>(Kt + (8 * c8 + 2 * e + 1) * L::LDKT + 2 * pr) = hi;
-                }
-            }
-        }
-        sync_lds();
-
-        // ================= S <- e_last S + K^T diag(G_last) U
+        // S <- e_last S + K^T diag(G_last) U
         {
-            Frag dh[KBT][CT], dl[KBT][CT];
+            const float gam_c = gE[CH - 1];
+            Frag dh[KBT], dl[KBT];
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
-                const f32x4 lr4 = *reinterpret_cast<const f32x4 *>(gL + 16 * tt + 4 * lg);
+                const f32x4 l4 = *reinterpret_cast<const f32x4 *>(gL + 16 * tt + 4 * lg);
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) U[tt][ct][i] *= lr4[i];
+                for (int i = 0; i < 4; ++i) U[tt][i] *= l4[i];
             }
 #pragma unroll
-            for (int kb = 0; kb < KBT; ++kb)
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    if constexpr (P::kBF16) bfrag_split(U[2 * kb][ct], U[2 * kb + 1][ct], dh[kb][ct], dl[kb][ct]);
-                    else dh[kb][ct] = U[kb][ct];
-                }
+            for (int kb = 0; kb < KBT; ++kb) {
+                if constexpr (P::kBF16) bfrag_split(U[2 * kb], U[2 * kb + 1], dh[kb], dl[kb]);
+                else dh[kb] = U[kb];
+            }
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
+                f32x4 s = S[rt] * gam_c;
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    f32x4 s = S[rt][ct] * gam_c;
-#pragma unroll
-                    for (int kb = 0; kb < KBT; ++kb) {
-                        if constexpr (P::kBF16) {
-                            const Frag kf = frag_rows(Kt, L::LDKT, 16 * rt, kb, lane);
-                            s = mma(s, kf, dh[kb][ct]);
-                            s = mma(s, kf, dl[kb][ct]);
-                        } else {
-                            s = mma(s, frag_cols(reinterpret_cast<const float *>(Ks), L::LDK, 16 * rt, kb, lane),
-                                    dh[kb][ct]);
-                        }
+                for (int kb = 0; kb < KBT; ++kb) {
+                    if constexpr (P::kBF16) {
+                        const Frag kf = frag_rows(Kt, L::LDKT, 16 * rt, kb, lane);
+                        s = mma(s, kf, dh[kb]);
+                        s = mma(s, kf, dl[kb]);
+                    } else {
+                        s = mma(s, frag_cols(reinterpret_cast<const float *>(Ks), L::LDK, 16 * rt, kb, lane), dh[kb]);
                     }
-                    S[rt][ct] = s;
                 }
-                    }
-        }
-        // row-contiguous store of the staged outputs (rows < len)
-        if constexpr (WITH_O) {
-            if (a.o_out && !a.o_f32) {
-                E *og = reinterpret_cast<E *>(a.o_out);
-#pragma unroll
-                for (int j = 0; j < (CH * NVO + NTHR - 1) / NTHR; ++j) {
-                    const int e = tid + j * NTHR;
-                    const int rr = e / NVO, vc = e % NVO;
-                    if (e < CH * NVO && rr < len)
-                        *reinterpret_cast<u32x4 *>(og + ((obase + rr) * a.h_v + h) * DV + cb * W + VEC * vc) =
-                            *reinterpret_cast<const u32x4 *>(Os + rr * L::LDO + VEC * vc);
-                }
+                S[rt] = s;
             }
+        }
+    }
+    if constexpr (WITH_O) {
+        if (opend >= 0) {
+            sync_lds();
+            store_o<E, DV, W, NVO, NTHR, L::LDO>(a, Os, opend, olen, h, cb, tid);
         }
     }
 
@@ -789,10 +718,8 @@ __global__ void __launch_bounds__(64 * (W / 16)) gdn_chunk_kernel(ChunkArgs a)
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a.S_out[sbase + (int64_t)(16 * rt + 4 * lg + i) * DV + col0 + 16 * ct + lr] = S[rt][ct][i];
+        for (int i = 0; i < 4; ++i)
+            a.S_out[sbase + (int64_t)(16 * rt + 4 * lg + i) * DV + col0 + lr] = S[rt][i];
 }
 
 template <int DK, int DV, int W, class P, bool WITH_O>
