@@ -74,3 +74,37 @@ def compare(inp: dict, mode: str, S_gpu, o_gpu, S_ref, o_ref):
                 eo = max(eo, _rel(o_g[start:start + cnt, h], o_ref[start:start + cnt, h]))
             row += cnt
     return eS, eo
+
+
+def rel(a, b):
+    return _rel(np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64))
+
+
+def sampled_refs(inp: dict, pairs, mode: str, with_o=True):
+    """Oracle states (and outputs) of sampled (sequence, v-head) chains of a large
+    workload, computed in one threaded oracle call with the chains packed as
+    one-head sequences.  Replay of a window from zero = prefill of that window."""
+    parts = [oracle.chain_inputs(inp, n, h, mode) for (n, h) in pairs]
+    lens = [p[0].shape[0] for p in parts]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    cat = [np.concatenate([p[i] for p in parts]) for i in range(5)]
+    S, o = oracle.prefill(*cat, cu, scale=inp["workload"].scale, want_o=with_o)
+    outs = []
+    for j in range(len(pairs)):
+        outs.append((S[j, 0], o[cu[j]:cu[j + 1], 0] if o is not None else None))
+    return outs
+
+
+def sampled_compare(inp: dict, mode: str, S_gpu, o_gpu, cu_out, pairs):
+    """Max relative errors of S and o over sampled (sequence, head) chains."""
+    refs = sampled_refs(inp, pairs, mode, with_o=o_gpu is not None)
+    eS, eo = 0.0, 0.0
+    for (n, h), (Sr, orf) in zip(pairs, refs):
+        eS = max(eS, rel(oracle.widen(S_gpu[n, h]), Sr))
+        if o_gpu is not None:
+            if mode == "replay":
+                r0 = int(cu_out[n]); cnt = int(inp["r_host"][n])
+            else:
+                r0 = int(inp["cu_host"][n]); cnt = int(inp["cu_host"][n + 1] - inp["cu_host"][n])
+            eo = max(eo, rel(oracle.widen(o_gpu[r0:r0 + cnt, h]), orf))
+    return eS, eo

@@ -1,0 +1,202 @@
+"""GPU edge cases, invariants and the error report, against the fp64 oracle.
+
+Tolerances: relative Frobenius error of S and o <= 1e-5 (fp32 inputs), <= 3e-3
+(bf16 inputs, fp32 state), max over (sequence, v-head).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_helpers import TOL, compare, gpu_run, oracle_run, rel, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import gated_deltanet_state_gdn_amd as gdn
+    gdn.load()
+    yield
+
+
+def _case(w, mode="replay", **kw):
+    inp = W.make_inputs(w)
+    say("case", w.name, mode, "L", list(w.lengths), "r", list(w.replay), kw)
+    S, o, cu_out = gpu_run(to_dev(inp), mode, **kw)
+    torch.cuda.synchronize()
+    S_ref, o_ref = oracle_run(inp, mode, with_o=o is not None)
+    eS, eo = compare(inp, mode, S, o, S_ref, o_ref)
+    say("  relerr S %.3e  o %.3e" % (eS, eo))
+    return inp, S, o, cu_out, eS, eo
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_varlen_ragged_and_degenerate(dtype):
+    # empty sequences, r = 0, r = 1, L < 64, L = 64, L = 65, partial last chunks
+    L = [0, 1, 63, 64, 65, 130, 200, 5]
+    r = [0, 1, 1, 64, 65, 7, 200, 0]
+    if dtype == "bf16":
+        w = W.small(W.config(2), L=L, r=r, h_qk=2, h_v=4)
+    else:
+        w = W.small(W.config(0), L=L, r=r)
+    for mode in ("replay", "prefill"):
+        inp, S, o, cu_out, eS, eo = _case(w, mode)
+        assert eS <= TOL[w.dtype] and eo <= TOL[w.dtype]
+        if mode == "replay":
+            Sg = S.cpu()
+            for n in range(len(L)):
+                if r[n] == 0:
+                    assert torch.count_nonzero(Sg[n]) == 0      # Zero-Only: S = 0 exactly
+            assert np.array_equal(cu_out.cpu().numpy(), np.concatenate([[0], np.cumsum(r)]))
+
+
+def test_replay_full_window_is_prefill_bitwise():
+    w = W.small(W.config(1), L=[300, 64, 129], r=[300, 64, 129], h_qk=4, h_v=4)
+    inp = to_dev(W.make_inputs(w))
+    S1, o1, _ = gpu_run(inp, "replay")
+    S2, o2, _ = gpu_run(inp, "prefill")
+    torch.cuda.synchronize()
+    assert torch.equal(S1, S2) and torch.equal(o1, o2)
+
+
+def test_deterministic_repeat():
+    w = W.small(W.config(2), L=[500, 333], r=[301, 333], h_qk=2, h_v=4)
+    inp = to_dev(W.make_inputs(w))
+    runs = [gpu_run(inp, "replay") for _ in range(3)]
+    torch.cuda.synchronize()
+    for S, o, _ in runs[1:]:
+        assert torch.equal(S, runs[0][0]) and torch.equal(o, runs[0][1])
+
+
+def test_state_only_matches_with_outputs():
+    w = W.small(W.config(1), L=[400], r=[250], h_qk=4, h_v=4)
+    inp = to_dev(W.make_inputs(w))
+    S1, _, _ = gpu_run(inp, "replay", with_o=True)
+    S2, o2, _ = gpu_run(inp, "replay", with_o=False)
+    torch.cuda.synchronize()
+    assert o2 is None
+    assert torch.equal(S1, S2)
+
+
+def test_fp32_outputs_for_bf16_inputs():
+    w = W.small(W.config(1), L=[300], r=[200], h_qk=2, h_v=2)
+    inp, S, o, _, eS, eo = _case(w, "replay", o_dtype=torch.float32)
+    assert o.dtype == torch.float32
+    assert eS <= 3e-3 and eo <= 3e-3
+
+
+def test_scale():
+    w = W.small(W.config(1), L=[200], r=[150], h_qk=2, h_v=2, scale=0.125)
+    inp, S, o, _, eS, eo = _case(w, "replay")
+    assert eS <= 3e-3 and eo <= 3e-3
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 128)])
+def test_fp32_wide_values(dk, dv):
+    # fp32 inputs with d_v = 128 run as two column blocks per head
+    w = W.small(W.config(0), L=[300], r=[170], d_k=dk, d_v=dv)
+    inp, S, o, _, eS, eo = _case(w, "replay")
+    assert eS <= 1e-5 and eo <= 1e-5
+
+
+def test_resets_inside_and_before_window():
+    # alpha = 0 tokens (g = -inf): one per head at random positions, and forced inside
+    # the window in a second case, where replay must equal full prefill.
+    w = W.small(W.config(4), L=[700], r=[300], h_qk=4, h_v=4, reset_heads=True)
+    inp, S, o, _, eS, eo = _case(w, "replay")
+    assert eS <= 3e-3 and eo <= 3e-3
+    inp, S, o, _, eS, eo = _case(w, "prefill")
+    assert eS <= 3e-3 and eo <= 3e-3
+    # with the alpha = 0 token inside the window the replayed state equals the full
+    # prefill state exactly (oracle), so the GPU replay must match the full state
+    w2 = w.with_(reset_in_window=True)
+    inp2 = W.make_inputs(w2)
+    Sr, _, _ = gpu_run(to_dev(inp2), "replay")
+    torch.cuda.synchronize()
+    S_full, _ = oracle_run(inp2, "prefill", with_o=False)
+    S_rep, _ = oracle_run(inp2, "replay", with_o=False)
+    assert np.array_equal(S_full, S_rep)
+    for h in range(4):
+        e = rel(oracle.widen(Sr[0, h]), S_full[0, h])
+        say("  reset in window, head %d: relerr(GPU replay, full) %.3e" % (h, e))
+        assert e <= 3e-3
+
+
+def test_resets_at_chunk_boundaries():
+    w = W.small(W.config(1), L=[320], r=[320], h_qk=2, h_v=2)
+    inp = W.make_inputs(w)
+    for p in (0, 63, 64, 127, 128, 200, 201, 319):
+        inp["g"][p, p % 2] = float("-inf")
+    S, o, _ = gpu_run(to_dev(inp), "prefill")
+    torch.cuda.synchronize()
+    S_ref, o_ref = oracle_run(inp, "prefill")
+    eS, eo = compare(inp, "prefill", S, o, S_ref, o_ref)
+    say("  resets at chunk edges: relerr S %.3e o %.3e" % (eS, eo))
+    assert np.isfinite(eS) and eS <= 3e-3 and eo <= 3e-3
+
+
+def test_prefill_from_initial_state_composition():
+    # prefill(0..m) then prefill(m..L, S0 = S_m) equals prefill(0..L) (within tolerance)
+    w = W.small(W.config(2), L=[400], r=[400], h_qk=2, h_v=4)
+    inp = W.make_inputs(w)
+    m = 150
+    import gated_deltanet_state_gdn_amd as gdn
+    d = to_dev(inp)
+    cu1 = torch.tensor([0, m], dtype=torch.int32, device="cuda")
+    cu2 = torch.tensor([0, 400 - m], dtype=torch.int32, device="cuda")
+    sl1, sl2 = slice(0, m), slice(m, 400)
+    S1, _ = gdn.gdn_prefill(d["q"][sl1], d["k"][sl1], d["v"][sl1], d["g"][sl1], d["beta"][sl1], cu1)
+    S2, o2 = gdn.gdn_prefill(d["q"][sl2], d["k"][sl2], d["v"][sl2], d["g"][sl2], d["beta"][sl2], cu2, S0=S1)
+    torch.cuda.synchronize()
+    S_ref, o_ref = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], [0, 400])
+    for h in range(4):
+        eS = rel(oracle.widen(S2[0, h]), S_ref[0, h])
+        eo = rel(oracle.widen(o2[:, h]), o_ref[m:, h])
+        say("  head %d composition relerr S %.3e o %.3e" % (h, eS, eo))
+        assert eS <= 3e-3 and eo <= 3e-3
+
+
+def test_relerr_kernel_against_host():
+    import gated_deltanet_state_gdn_amd as gdn
+    g = torch.Generator().manual_seed(5)
+    A = torch.randn((3, 5, 128, 128), generator=g)
+    B = A + 1e-3 * torch.randn(A.shape, generator=g)
+    B[1, 2] = 0.0
+    A[2, 3, 7, 9] = float("nan")
+    rel_d, nf_d = gdn.gdn_state_relerr(A.cuda(), B.cuda())
+    torch.cuda.synchronize()
+    ref, _ = oracle.state_relerr(A.numpy(), B.numpy())
+    got = rel_d.cpu().numpy()
+    ok = np.isfinite(ref)
+    assert np.allclose(got[ok], ref[ok], rtol=1e-5, atol=0)
+    assert np.isnan(got[2, 3])
+    nf = nf_d.cpu().numpy()
+    assert nf[2, 3] == 1 and nf.sum() == 1
+    # reference norm 0 -> absolute norm
+    assert abs(got[1, 2] - np.linalg.norm(A[1, 2].numpy())) <= 1e-5 * np.linalg.norm(A[1, 2].numpy())
+
+
+def test_device_status_reports_bad_device_inputs():
+    import gated_deltanet_state_gdn_amd as gdn
+    w = W.small(W.config(1), L=[100, 50], r=[30, 20], h_qk=2, h_v=2)
+    d = to_dev(W.make_inputs(w))
+    desc = gdn.make_desc(d["q"], d["v"], 2, 50)
+    ws = gdn.workspace(desc, "cuda")
+    gdn.gdn_replay(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["r"],
+                   total_out_tokens=50, ws=ws)
+    assert gdn.gdn_device_status(ws) == 0
+    bad_r = torch.tensor([30, 51], dtype=torch.int32, device="cuda")        # r > L
+    gdn.gdn_replay(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], bad_r,
+                   total_out_tokens=81, ws=ws)
+    assert gdn.gdn_device_status(ws) == 8
+    bad_cu = torch.tensor([0, 120, 100], dtype=torch.int32, device="cuda")  # non-monotone
+    gdn.gdn_replay(d["q"], d["k"], d["v"], d["g"], d["beta"], bad_cu, d["r"],
+                   total_out_tokens=50, ws=ws)
+    assert gdn.gdn_device_status(ws) == 8
+    short_out = torch.tensor([30, 20], dtype=torch.int32, device="cuda")   # sum r > rows of o
+    gdn.gdn_replay(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], short_out,
+                   total_out_tokens=40, ws=ws)
+    assert gdn.gdn_device_status(ws) == 8
