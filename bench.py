@@ -58,7 +58,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-extra", action="store_true", help="skip prefill / per-layer timings")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, max(1, args.steps))
+        return
 
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus %d is not supported "
@@ -144,7 +149,7 @@ def main():
                    "state": "fp32"},
         "rebuild_us_per_layer": kern_ms * 1e3 / layers,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profile(kern_ms),
                      "algorithmic_bytes_per_launch": abytes, "kernel_ms": kern_ms,
                      "algorithmic_tflops": aflops / (kern_ms * 1e-3) / 1e12},
     }
@@ -195,6 +200,36 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, inp, with_o, args.cpu_seconds)
 
     print(json.dumps(out), flush=True)
+
+
+def copy_calibration(mib: int, reps: int):
+    """A plain device-to-device copy of known size (the scale for FETCH_SIZE/WRITE_SIZE)."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n,
+                      "launches": reps}), flush=True)
+
+
+def traffic_from_profile(kernel_ms):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    kernel source as it is now (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gdn_chunk_traffic.json")
+    src = os.path.join(ROOT, "gated_deltanet_state_gdn_amd", "csrc", "gdn_chunk.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(w, inp, with_o, budget_s):
