@@ -93,8 +93,8 @@ int32_t run(const gdn_desc *d, const void *q, const void *k, const void *v, cons
     a.n_seqs = d->n_seqs; a.h_qk = d->h_qk; a.h_v = d->h_v;
     a.o_f32 = (d->o_dtype == GDN_F32 && d->qkv_dtype == GDN_BF16) ? 1 : 0;
     a.scale = d->scale;
-    const hipError_t e = gdn::launch_chunk(a, d->qkv_dtype == GDN_BF16, d->d_k, d->d_v,
-                                           o_out != nullptr, reinterpret_cast<hipStream_t>(stream));
+    const hipError_t e = gdn::launch_chunk_ws(a, d->qkv_dtype == GDN_BF16, d->d_k, d->d_v,
+                                              o_out != nullptr, reinterpret_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported) return GDN_ERR_UNSUPPORTED;
     return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }

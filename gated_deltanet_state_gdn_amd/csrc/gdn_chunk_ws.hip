@@ -1,0 +1,743 @@
+// Chunked gated delta rule (replay and prefill) for gfx950 / CDNA4.
+//
+// The recurrence (Gated DeltaNet, as replayed by Tail-Replay over the last r tokens
+// of a matched prefix from a zero state; gist.science technical summary,
+// "Mecanismos Principais"):
+//     S_t = a_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T,   o_t = scale S_t^T q_t
+// is evaluated in chunks of C = 64 tokens.  For one chunk with incoming state S:
+//     H_i  cumulative log-gate since the last a = 0 token,  e_i = exp(H_i) (0 after a reset)
+//     G_ij = exp(H_i - H_j) if no reset in (j, i], else 0             (j <= i)
+//     A    = strict_lower(diag(b) (K K^T o G))
+//     (I + A) U = Y,  Y = diag(b) (V - diag(e) K S)                     (UT transform)
+//     O    = scale (diag(e) Q S + lower(Q K^T o G) U)
+//     S   <- e_last S + K^T diag(G_last,.) U
+// which equals the token recurrence exactly in exact arithmetic.  The triangular
+// solve runs as forward substitution over 16-row blocks,
+//     U_b = Z_b + (T_bb - I) Z_b,   Z_b = Y_b - sum_{j<b} A_bj U_j,   T_bb = (I + A_bb)^{-1}.
+//
+// Work decomposition: one workgroup per (sequence, v-head, d_v block), split into two
+// roles that run concurrently on double-buffered LDS:
+//   * state waves (one per 16-column tile of S): the sequential pass over the chunks.
+//     S never leaves their MFMA accumulators; the columns of S evolve independently
+//     because (I - b k k^T) acts on the d_k side only, so they exchange nothing.
+//   * four prep waves: everything that does not depend on S, one chunk ahead -- the
+//     chunk's K, Q (and K^T) in LDS, the gate scan, the Gram products forming -A and
+//     P, and the diagonal-block inverses.
+// One workgroup barrier per chunk hands a prepared buffer to the state waves; the
+// prep waves order their own steps with a counter in LDS.
+//
+// Precision (bf16 inputs, fp32 state): q/k/v enter MFMA exactly; the gates, b, the
+// unit diagonal of the solve and the diagonal of P are applied in fp32; S enters Q S
+// as hi + lo bf16 (hi in K S); U enters P U and K^T U as hi + lo; P as hi + lo;
+// A_bj, T_bb - I and Z as bf16.  fp32 inputs use fp32 MFMA throughout.
+//
+// Matrix-core layout used (16x16 MFMA): lane l supplies row l%16 of A and column
+// l%16 of B; element j of lane group l/16 in A pairs with element j of the same
+// lane group in B; the accumulator holds D[4*(l/16)+i][l%16] in element i.  A
+// fragment whose contraction indices follow the accumulator rows lets a D tile be
+// used directly as a B operand (S in K S and Q S, Z/U in the solve, U in P U and
+// K^T U).
+#include <type_traits>
+
+#include "gdn_common.h"
+
+namespace gdn {
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr int CH = 64;       // chunk length (tokens)
+constexpr int NPW = 4;       // prep waves per workgroup
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    __bf16 h = (__bf16)f;                  // round to nearest even (v_cvt_pk_bf16_f32)
+    return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// ---------------------------------------------------------------- policies
+struct PolF32 {
+    static constexpr bool kBF16 = false;
+    static constexpr int KB = 16;    // contraction length of one fragment step
+    typedef float E;                 // element type of q/k/v and of LDS operands
+    typedef f32x4 Frag;
+};
+struct PolBF16 {
+    static constexpr bool kBF16 = true;
+    static constexpr int KB = 32;
+    typedef uint16_t E;
+    typedef bf16x8 Frag;
+};
+
+__device__ __forceinline__ f32x4 mma(f32x4 c, f32x4 a, f32x4 b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+    return c;
+}
+__device__ __forceinline__ f32x4 mma(f32x4 c, bf16x8 a, bf16x8 b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- LDS layouts
+// Row-major matrices with padded rows (RS bytes per row, 16 more than the data) so
+// that the 16 rows a fragment reads land on different banks; every fragment of a
+// matrix then shares one lane-dependent base address plus a constant offset.
+// A-operand fragment (or B = M^T): lane l gives row r0 + l%16 and the contraction
+// indices {4*(l/16) + i} (+16 for bf16) of k-block kb.
+template <int RS>
+__device__ __forceinline__ bf16x8 frag_rm(const char *M, int r0, int kb, int lane, uint16_t) {
+    const char *p = M + (r0 + (lane & 15)) * RS + kb * 64 + 8 * (lane >> 4);
+    const u32x2 a = *reinterpret_cast<const u32x2 *>(p);
+    const u32x2 b = *reinterpret_cast<const u32x2 *>(p + 32);
+    const u32x4 u = {a.x, a.y, b.x, b.y};
+    return __builtin_bit_cast(bf16x8, u);
+}
+template <int RS>
+__device__ __forceinline__ f32x4 frag_rm(const char *M, int r0, int kb, int lane, float) {
+    return *reinterpret_cast<const f32x4 *>(M + (r0 + (lane & 15)) * RS + kb * 64 + 16 * (lane >> 4));
+}
+// fp32 fragment of M^T for a row-major fp32 matrix whose rows are the contraction
+// index: lane l gives column c0 + l%16, rows kb*16 + 4*(l/16) + i.
+template <int RS>
+__device__ __forceinline__ f32x4 frag_rm_cols(const char *M, int c0, int kb, int lane) {
+    const char *p = M + (kb * 16 + 4 * (lane >> 4)) * RS + 4 * (c0 + (lane & 15));
+    f32x4 f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = *reinterpret_cast<const float *>(p + i * RS);
+    return f;
+}
+
+// 16x16 tiles, row-major (32-byte rows in bf16, 64-byte rows in fp32).  Lower-triangular
+// tile (ti >= tj) of a 64x64 matrix lives at index ti*(ti+1)/2 + tj.
+__device__ __forceinline__ int tri_index(int ti, int tj) { return ti * (ti + 1) / 2 + tj; }
+
+// Half fragment (4 contraction indices) from a tile, or zeros when tile < 0.
+__device__ __forceinline__ u32x2 tile_half(const uint16_t *T, int tile, int lane) {
+    if (tile < 0) return u32x2{0u, 0u};
+    return *reinterpret_cast<const u32x2 *>(T + tile * 256 + (lane & 15) * 16 + 4 * (lane >> 4));
+}
+// bf16 A fragment for k-block kb of tile row ti: tiles (ti, 2kb) and (ti, 2kb + 1);
+// ta, tb are tile indices or -1 for a zero half.
+__device__ __forceinline__ bf16x8 frag_tiles(const uint16_t *T, int ta, int tb, int lane) {
+    const u32x2 a = tile_half(T, ta, lane), b = tile_half(T, tb, lane);
+    const u32x4 u = {a.x, a.y, b.x, b.y};
+    return __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ f32x4 frag_tile(const float *T, int tile, int lane) {
+    return *reinterpret_cast<const f32x4 *>(T + tile * 256 + (lane & 15) * 16 + 4 * (lane >> 4));
+}
+
+// ---------------------------------------------------------------- B operands
+__device__ __forceinline__ bf16x8 bfrag_hi(const f32x4 &t0, const f32x4 &t1) {
+    const u32x4 u = {pack2(t0[0], t0[1]), pack2(t0[2], t0[3]), pack2(t1[0], t1[1]),
+                     pack2(t1[2], t1[3])};
+    return __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ void bfrag_split(const f32x4 &t0, const f32x4 &t1, bf16x8 &hi,
+                                            bf16x8 &lo) {
+    float h[8], r[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        h[i] = bf2f(f2bf(t0[i]));
+        h[4 + i] = bf2f(f2bf(t1[i]));
+        r[i] = t0[i] - h[i];
+        r[4 + i] = t1[i] - h[4 + i];
+    }
+    const u32x4 uh = {pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
+    const u32x4 ul = {pack2(r[0], r[1]), pack2(r[2], r[3]), pack2(r[4], r[5]), pack2(r[6], r[7])};
+    hi = __builtin_bit_cast(bf16x8, uh);
+    lo = __builtin_bit_cast(bf16x8, ul);
+}
+
+__device__ __forceinline__ void st_e(float *p, float x) { *p = x; }
+__device__ __forceinline__ void st_e(uint16_t *p, float x) { *p = f2bf(x); }
+
+// V held in registers between its load and Y, one element per register.
+template <class P> struct VHold {
+    typedef typename std::conditional<P::kBF16, uint32_t, float>::type T;
+};
+template <class P>
+__device__ __forceinline__ float v_at(typename VHold<P>::T v) {
+    if constexpr (P::kBF16) return __uint_as_float(v << 16);
+    else return v;
+}
+
+// Lower-triangular 16x16 tile list of a 64x64 product (ti >= tj).
+__device__ __forceinline__ void tri_tile(int idx, int &ti, int &tj) {
+    // 0:(0,0) 1:(1,0) 2:(1,1) 3:(2,0) 4:(2,1) 5:(2,2) 6:(3,0) 7:(3,1) 8:(3,2) 9:(3,3)
+    ti = idx >= 6 ? 3 : idx >= 3 ? 2 : idx >= 1 ? 1 : 0;
+    tj = idx - (ti * (ti + 1)) / 2;
+}
+
+// Workgroup barrier that orders LDS only: global loads stay in flight across it
+// (a full __syncthreads also waits for every outstanding global load).
+__device__ __forceinline__ void sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Barrier among the prep waves only: each wave adds 1 to an LDS counter and waits
+// until every prep wave has; the target grows by NPW per use, so the counter is never
+// reset.  The wait is bounded: a wave that never arrived would only cost wrong results
+// (flagged in the status word), never a hang.
+__device__ __forceinline__ void prep_sync(int *ctr, int &target, int lane, int *fail) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    target += NPW;
+    if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    int spins = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > (1 << 24)) {
+            *fail = 1;
+            break;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ---------------------------------------------------------------- LDS plan
+// Two chunk buffers (the state waves read one while the prep waves fill the other),
+// then the prep waves' fp32 diagonal blocks of -A, then a few words.
+template <int DK, class P, bool WITH_O>
+struct Lds {
+    typedef typename P::E E;
+    static constexpr int RBK = DK * (int)sizeof(E);          // K / Q row bytes
+    static constexpr int RSK = RBK + 16;                       // padded K / Q row stride
+    static constexpr int RST = CH * 2 + 16;                    // padded K^T row stride (bf16)
+    static constexpr int TILE = 256 * (int)sizeof(E);          // one 16x16 tile
+    static constexpr int oGate = 0;                            // H, e, b, G_last, Pd, rho
+    static constexpr int oK = 6 * CH * 4;
+    static constexpr int oQ = oK + CH * RSK;
+    static constexpr int oKt = oQ + (WITH_O ? CH * RSK : 0);
+    static constexpr int oA = oKt + (P::kBF16 ? DK * RST : 0);     // 10 lower tiles of -A
+    static constexpr int oT = oA + 10 * TILE;                       // 4 tiles T_bb - I
+    static constexpr int oPh = oT + 4 * TILE;                       // 10 lower tiles of P
+    static constexpr int oPl = oPh + (WITH_O ? 10 * TILE : 0);      // bf16 low parts
+    static constexpr int BUF = oPl + ((WITH_O && P::kBF16) ? 10 * TILE : 0);
+    static constexpr int oDiag = 2 * BUF;                           // 4 x 16x16 fp32
+    static constexpr int oMisc = oDiag + 4 * 256 * 4;
+    static constexpr int bytes = oMisc + 64;
+};
+
+template <class P, int KBK, int RSK>
+__device__ __forceinline__ f32x4 gram16(const char *Am, const char *Bm, int ti, int tj, int lane) {
+    f32x4 gr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KBK; ++kb)
+        gr = mma(gr, frag_rm<RSK>(Am, 16 * ti, kb, lane, typename P::E()),
+                 frag_rm<RSK>(Bm, 16 * tj, kb, lane, typename P::E()));
+    return gr;
+}
+
+// ---------------------------------------------------------------- kernel
+template <int DK, int DV, int W, class P, bool WITH_O>
+__global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(ChunkArgs a)
+{
+    constexpr int NSW = W / 16;            // state waves: one 16-column tile of S each
+    constexpr int NTHR = 64 * (NSW + NPW);
+    typedef typename P::E E;
+    typedef typename P::Frag Frag;
+    typedef Lds<DK, P, WITH_O> L;
+    constexpr int RT = DK / 16;            // row tiles of S
+    constexpr int KBK = DK / P::KB;        // k-blocks over d_k
+    constexpr int KBT = CH / P::KB;        // k-blocks over the chunk's tokens
+    constexpr int NCB = DV / W;            // column blocks per head
+    constexpr int RBK = L::RBK, RSK = L::RSK, RST = L::RST;
+    static_assert(L::bytes <= 160 * 1024, "LDS plan");
+
+    __shared__ __attribute__((aligned(16))) char smem[L::bytes];
+    float *diag = reinterpret_cast<float *>(smem + L::oDiag);
+    int64_t *gMisc = reinterpret_cast<int64_t *>(smem + L::oMisc);
+    int *pctr = reinterpret_cast<int *>(smem + L::oMisc + 8);
+    int *pfail = reinterpret_cast<int *>(smem + L::oMisc + 12);
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane0 = tid & 63;
+    int lane = lane0, lr = lane & 15, lg = lane >> 4;
+    const bool is_state = wave < NSW;
+
+    // ---- block -> (sequence, v-head, column block); XCD-aware: consecutive logical
+    // blocks (the v-heads of one q/k head, the heads of one sequence) share an XCD's L2.
+    const int64_t nblk = (int64_t)gridDim.x;
+    int64_t bid = blockIdx.x;
+    if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+    const int cb = (int)(bid % NCB);
+    const int h = (int)((bid / NCB) % a.h_v);
+    const int n = (int)(bid / ((int64_t)NCB * a.h_v));
+    const int hk = (int)(((int64_t)h * a.h_qk) / a.h_v);
+    const bool replay = a.r != nullptr;
+
+    // ---- window selection (validates the device-resident cu_seqlens / r)
+    if (bid == 0) {
+        int bad = 0;
+        for (int m = tid; m < a.n_seqs; m += NTHR) {
+            const int64_t b0 = a.cu[m], b1 = a.cu[m + 1];
+            if (b0 < 0 || b1 < b0 || b1 > a.total_tokens) bad = 1;
+            if (replay && (a.r[m] < 0 || a.r[m] > b1 - b0)) bad = 1;
+        }
+        if (replay && wave == 0) {   // the packed outputs must fit o_out
+            int64_t tot = 0;
+            for (int m = lane; m < a.n_seqs; m += 64) tot += a.r[m];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
+            if (tot > a.total_out) bad = 1;
+        }
+        bad = __syncthreads_or(bad);
+        if (tid == 0) *a.status = bad ? kStatusBadInput : kStatusOk;
+    }
+    const int64_t beg = a.cu[n], end = a.cu[n + 1];
+    if (beg < 0 || end < beg || end > a.total_tokens) return;
+    const int64_t rn = replay ? (int64_t)a.r[n] : end - beg;
+    if (rn < 0 || rn > end - beg) return;
+    const int64_t wbeg = end - rn;              // first token of the window
+    if (wave == 0) {
+        int64_t row0 = beg;
+        if (replay) {
+            int64_t s = 0;
+            for (int m = lane; m < n; m += 64) s += a.r[m];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+            row0 = s;
+        }
+        if (lane == 0) {
+            gMisc[0] = row0;
+            *pctr = 0;
+            *pfail = 0;
+        }
+    }
+    __syncthreads();
+    const int64_t orow0 = gMisc[0];
+    if (orow0 < 0 || orow0 + rn > (replay ? a.total_out : a.total_tokens)) return;
+    if (a.cu_out && h == 0 && cb == 0 && tid == 0) {
+        a.cu_out[n] = (int32_t)orow0;
+        if (n == a.n_seqs - 1) a.cu_out[n + 1] = (int32_t)(orow0 + rn);
+    }
+    const int64_t nch = (rn + CH - 1) / CH;
+
+    const E *qg = reinterpret_cast<const E *>(a.q);
+    const E *kg = reinterpret_cast<const E *>(a.k);
+    const E *vg = reinterpret_cast<const E *>(a.v);
+    const int64_t sbase = ((int64_t)n * a.h_v + h) * DK * DV;
+
+    if (is_state) {
+        // =====================================================================
+        // state waves
+        const int col0 = cb * W + wave * 16;       // first d_v column of this wave
+        f32x4 S[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            if (!replay && a.S0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    S[rt][i] = a.S0[sbase + (int64_t)(16 * rt + 4 * lg + i) * DV + col0 + lr];
+            } else {
+                S[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        // V rows of a chunk in accumulator layout; rows past the chunk end read the
+        // last valid row (finite; their b is 0, so they never contribute)
+        typename VHold<P>::T vreg[4][4];
+        auto fetch_v = [&](int64_t cc) {
+            const int ln = (int)((rn - cc) < CH ? (rn - cc) : CH);
+            const int64_t tb = wbeg + cc;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = min(16 * tt + 4 * lg + i, ln - 1);
+                    const E x = vg[((tb + row) * a.h_v + h) * DV + col0 + lr];
+                    if constexpr (P::kBF16) vreg[tt][i] = (uint32_t)x;
+                    else vreg[tt][i] = x;
+                }
+        };
+        if (nch > 0) fetch_v(0);
+        sync_lds();                                  // chunk 0 prepared
+
+        for (int64_t c = 0; c < nch; ++c) {
+            const int64_t c0 = c * CH;
+            const int len = (int)((rn - c0) < CH ? (rn - c0) : CH);
+            // lane-derived indices are recomputed each chunk instead of being held in
+            // registers across the whole loop
+            int lane = lane0;
+            asm volatile("" : "+v"(lane));
+            const int lr = lane & 15, lg = lane >> 4;
+            const char *buf = smem + (c & 1) * L::BUF;
+            const char *Ks = buf + L::oK;
+            const char *Qs = buf + L::oQ;
+            const float *gH = reinterpret_cast<const float *>(buf + L::oGate);
+            const float *gE = gH + CH, *gB = gE + CH, *gL = gB + CH, *gPd = gL + CH;
+
+            // X = K S (S as hi bf16) and Q S (S as hi + lo), k-block by k-block
+            f32x4 X[4], QS[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                X[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                QS[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int kb = 0; kb < KBK; ++kb) {
+                Frag sh, sl;
+                if constexpr (P::kBF16) bfrag_split(S[2 * kb], S[2 * kb + 1], sh, sl);
+                else sh = S[kb];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    X[tt] = mma(X[tt], frag_rm<RSK>(Ks, 16 * tt, kb, lane, E()), sh);
+                    if constexpr (WITH_O) {
+                        const Frag qf = frag_rm<RSK>(Qs, 16 * tt, kb, lane, E());
+                        QS[tt] = mma(QS[tt], qf, sh);
+                        if constexpr (P::kBF16) QS[tt] = mma(QS[tt], qf, sl);
+                    }
+                }
+            }
+            // Y = b (V - e X), in place
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const f32x4 br = *reinterpret_cast<const f32x4 *>(gB + 16 * tt + 4 * lg);
+                const f32x4 er = *reinterpret_cast<const f32x4 *>(gE + 16 * tt + 4 * lg);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) X[tt][i] = br[i] * (v_at<P>(vreg[tt][i]) - er[i] * X[tt][i]);
+            }
+            if (c + 1 < nch) fetch_v(c0 + CH);       // lands while this chunk is processed
+
+            // (I + A) U = Y by 16-row block forward substitution
+            f32x4 U[4];
+            if constexpr (P::kBF16) {
+                const uint16_t *At = reinterpret_cast<const uint16_t *>(buf + L::oA);
+                const uint16_t *Tt = reinterpret_cast<const uint16_t *>(buf + L::oT);
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    f32x4 z = X[b];
+                    if (b >= 1) {   // tiles (b, 0), (b, 1); U_1 is still zero when b = 1
+                        z = mma(z, frag_tiles(At, tri_index(b, 0), tri_index(b, 1), lane),
+                                bfrag_hi(U[0], b >= 2 ? U[1] : zero));
+                        if (b == 3)
+                            z = mma(z, frag_tiles(At, tri_index(3, 2), tri_index(3, 3), lane),
+                                    bfrag_hi(U[2], zero));
+                    }
+                    const bool odd = (b & 1) != 0;
+                    U[b] = mma(z, frag_tiles(Tt, odd ? -1 : b, odd ? b : -1, lane),
+                               odd ? bfrag_hi(zero, z) : bfrag_hi(z, zero));
+                }
+            } else {
+                const float *At = reinterpret_cast<const float *>(buf + L::oA);
+                const float *Tt = reinterpret_cast<const float *>(buf + L::oT);
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    f32x4 z = X[b];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (j < b) z = mma(z, frag_tile(At, tri_index(b, j), lane), U[j]);
+                    U[b] = mma(z, frag_tile(Tt, b, lane), z);
+                }
+            }
+
+            // O = e (Q S) + Pd U + P_off U   (QS registers become O), stored from registers
+            if constexpr (WITH_O) {
+                Frag uh[KBT], ul[KBT];
+#pragma unroll
+                for (int kb = 0; kb < KBT; ++kb) {
+                    if constexpr (P::kBF16) bfrag_split(U[2 * kb], U[2 * kb + 1], uh[kb], ul[kb]);
+                    else uh[kb] = U[kb];
+                }
+                const E *Ph = reinterpret_cast<const E *>(buf + L::oPh);
+                const E *Pl = reinterpret_cast<const E *>(buf + L::oPl);
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    const f32x4 er = *reinterpret_cast<const f32x4 *>(gE + 16 * tt + 4 * lg);
+                    const f32x4 pd = *reinterpret_cast<const f32x4 *>(gPd + 16 * tt + 4 * lg);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) QS[tt][i] = er[i] * QS[tt][i] + pd[i] * U[tt][i];
+#pragma unroll
+                    for (int kb = 0; kb < KBT; ++kb) {
+                        if (kb * P::KB < 16 * tt + 16) {
+                            if constexpr (P::kBF16) {
+                                const int ta = tri_index(tt, 2 * kb);
+                                const int tb = (2 * kb + 1 <= tt) ? tri_index(tt, 2 * kb + 1) : -1;
+                                const Frag ph = frag_tiles(Ph, ta, tb, lane);
+                                QS[tt] = mma(QS[tt], ph, uh[kb]);
+                                QS[tt] = mma(QS[tt], ph, ul[kb]);
+                                QS[tt] = mma(QS[tt], frag_tiles(Pl, ta, tb, lane), uh[kb]);
+                            } else {
+                                QS[tt] = mma(QS[tt], frag_tile(Ph, tri_index(tt, kb), lane), uh[kb]);
+                            }
+                        }
+                    }
+                }
+                if (a.o_out) {
+                    const int64_t obase = replay ? orow0 + c0 : wbeg + c0;
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int rr = 16 * tt + 4 * lg + i;
+                            if (rr < len) {
+                                const int64_t off = ((obase + rr) * a.h_v + h) * DV + col0 + lr;
+                                const float ov = a.scale * QS[tt][i];
+                                if (a.o_f32) reinterpret_cast<float *>(a.o_out)[off] = ov;
+                                else st_e(reinterpret_cast<E *>(a.o_out) + off, ov);
+                            }
+                        }
+                }
+            }
+
+            // S <- e_last S + K^T diag(G_last) U
+            {
+                const float gam_c = gE[CH - 1];
+                Frag dh[KBT], dl[KBT];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    const f32x4 l4 = *reinterpret_cast<const f32x4 *>(gL + 16 * tt + 4 * lg);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) U[tt][i] *= l4[i];
+                }
+#pragma unroll
+                for (int kb = 0; kb < KBT; ++kb) {
+                    if constexpr (P::kBF16) bfrag_split(U[2 * kb], U[2 * kb + 1], dh[kb], dl[kb]);
+                    else dh[kb] = U[kb];
+                }
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    f32x4 s = S[rt] * gam_c;
+#pragma unroll
+                    for (int kb = 0; kb < KBT; ++kb) {
+                        if constexpr (P::kBF16) {
+                            const Frag kf = frag_rm<RST>(buf + L::oKt, 16 * rt, kb, lane, uint16_t());
+                            s = mma(s, kf, dh[kb]);
+                            s = mma(s, kf, dl[kb]);
+                        } else {
+                            s = mma(s, frag_rm_cols<RSK>(Ks, 16 * rt, kb, lane), dh[kb]);
+                        }
+                    }
+                    S[rt] = s;
+                }
+            }
+            sync_lds();   // this chunk's buffer is free; the next one is prepared
+        }
+
+        // ---- state write-back
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a.S_out[sbase + (int64_t)(16 * rt + 4 * lg + i) * DV + col0 + lr] = S[rt][i];
+    } else {
+        // =====================================================================
+        // prep waves: chunk c + 1's operands while the state waves process chunk c
+        const int pw = wave - NSW;                 // 0..NPW-1
+        const int ptid = tid - 64 * NSW;           // 0..255
+        int target = 0;
+        constexpr int NVK = CH * RBK / 16;         // 16-byte vectors of a K (or Q) chunk
+        constexpr int NVT = NVK / (64 * NPW);      // per prep thread
+        constexpr int NCK = RBK / 16;              // vectors per row
+        static_assert(NVK % (64 * NPW) == 0, "vector map");
+        u32x4 kpf[NVT], qpf[NVT];
+        float gpf = 0.f, bpf = 0.f;
+        bool gok = false;
+        // rows past the chunk end load the last valid row: finite, and inert because
+        // their g and beta are set to 0 (alpha = 1, no write)
+        auto fetch = [&](int64_t cc) {
+            const int ln = (int)((rn - cc) < CH ? (rn - cc) : CH);
+            const int64_t tb = wbeg + cc;
+#pragma unroll
+            for (int j = 0; j < NVT; ++j) {
+                const int u = ptid + 64 * NPW * j;
+                const int row = min(u / NCK, ln - 1);
+                const int64_t off = ((tb + row) * a.h_qk + hk) * DK + (int64_t)(u % NCK) * (16 / sizeof(E));
+                kpf[j] = *reinterpret_cast<const u32x4 *>(kg + off);
+                if (WITH_O) qpf[j] = *reinterpret_cast<const u32x4 *>(qg + off);
+            }
+            if (pw == 0) {
+                const int64_t off = (tb + min(lane, ln - 1)) * a.h_v + h;
+                gpf = a.g[off];
+                bpf = a.beta[off];
+                gok = lane < ln;
+            }
+        };
+
+        auto prep = [&](int64_t cc) {
+            int lane = lane0;
+            asm volatile("" : "+v"(lane));
+            const int lr = lane & 15, lg = lane >> 4;
+            char *buf = smem + (cc & 1) * L::BUF;
+            char *Ks = buf + L::oK;
+            char *Qs = buf + L::oQ;
+            float *gH = reinterpret_cast<float *>(buf + L::oGate);
+            float *gE = gH + CH, *gB = gE + CH, *gL = gB + CH, *gPd = gL + CH;
+            int *gR = reinterpret_cast<int *>(gPd + CH);
+            // ---- step 1: K, Q into LDS; gate scan; fetch the chunk after
+#pragma unroll
+            for (int j = 0; j < NVT; ++j) {
+                const int u = ptid + 64 * NPW * j;
+                *reinterpret_cast<u32x4 *>(Ks + (u / NCK) * RSK + (u % NCK) * 16) = kpf[j];
+                if (WITH_O) *reinterpret_cast<u32x4 *>(Qs + (u / NCK) * RSK + (u % NCK) * 16) = qpf[j];
+            }
+            if (pw == 0) {
+                const float gv = gok ? gpf : 0.f, bv = gok ? bpf : 0.f;
+                // reset-aware inclusive scan: H = sum of g since the last alpha = 0 token
+                const bool reset = gv == -__builtin_inff();
+                float hv = reset ? 0.f : gv;
+                int seg = reset ? 1 : 0;
+                int rho = reset ? lane : -1;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float ho = __shfl_up(hv, off);
+                    const int so = __shfl_up(seg, off);
+                    const int ro = __shfl_up(rho, off);
+                    if (lane >= off) {
+                        if (!seg) hv += ho;
+                        seg |= so;
+                        rho = ro > rho ? ro : rho;
+                    }
+                }
+                const float hl = __shfl(hv, 63);
+                const int rl = __shfl(rho, 63);
+                gH[lane] = hv;
+                gE[lane] = rho < 0 ? __expf(hv) : 0.f;
+                gB[lane] = bv;
+                gR[lane] = rho;
+                gL[lane] = rl <= lane ? __expf(hl - hv) : 0.f;
+            }
+            if (cc + 1 < nch) fetch((cc + 1) * CH);
+            prep_sync(pctr, target, lane, pfail);
+
+            // ---- step 2: Gram tiles -> -A (tiles, and fp32 diagonal blocks for the
+            // inverses), P (hi + lo) and its diagonal; K^T
+            constexpr int NG = WITH_O ? 20 : 10;
+#pragma unroll
+            for (int j = 0; j < (NG + NPW - 1) / NPW; ++j) {
+                const int idx = pw + NPW * j;
+                if (idx < NG) {
+                    const bool isP = idx >= 10;
+                    int ti, tj;
+                    tri_tile(isP ? idx - 10 : idx, ti, tj);
+                    const f32x4 gr = gram16<P, KBK, RSK>(isP ? Qs : Ks, Ks, ti, tj, lane);
+                    const int c = 16 * tj + lr;
+                    const float hc = gH[c];
+                    const f32x4 hr = *reinterpret_cast<const f32x4 *>(gH + 16 * ti + 4 * lg);
+                    const f32x4 br = *reinterpret_cast<const f32x4 *>(gB + 16 * ti + 4 * lg);
+                    const int4 rr4 = *reinterpret_cast<const int4 *>(gR + 16 * ti + 4 * lg);
+                    const int rrs[4] = {rr4.x, rr4.y, rr4.z, rr4.w};
+                    const int tile = tri_index(ti, tj);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int rr = 16 * ti + 4 * lg + i;
+                        const float gam = (c < rr && rrs[i] <= c) ? __expf(hr[i] - hc) : 0.f;
+                        const int e = tile * 256 + (4 * lg + i) * 16 + lr;
+                        if (!isP) {
+                            const float na = -br[i] * gam * gr[i];
+                            st_e(reinterpret_cast<E *>(buf + L::oA) + e, na);
+                            if (ti == tj) diag[ti * 256 + (4 * lg + i) * 16 + lr] = na;
+                        } else if constexpr (WITH_O) {
+                            const float pv = gam * gr[i];
+                            if constexpr (P::kBF16) {
+                                const uint16_t hb = f2bf(pv);
+                                reinterpret_cast<uint16_t *>(buf + L::oPh)[e] = hb;
+                                reinterpret_cast<uint16_t *>(buf + L::oPl)[e] = f2bf(pv - bf2f(hb));
+                            } else {
+                                reinterpret_cast<float *>(buf + L::oPh)[e] = pv;
+                            }
+                            if (c == rr) gPd[rr] = gr[i];
+                        }
+                    }
+                }
+            }
+            if constexpr (P::kBF16) {
+                // K^T[dk][t] as packed token pairs: thread -> (token pair, 8-column block)
+                constexpr int NCB8 = DK / 8;
+#pragma unroll
+                for (int j = 0; j < (32 * NCB8) / (64 * NPW); ++j) {
+                    const int u = ptid + 64 * NPW * j;
+                    const int pr = u & 31, c8 = u >> 5;
+                    const u32x4 x0 = *reinterpret_cast<const u32x4 *>(Ks + (2 * pr) * RSK + 16 * c8);
+                    const u32x4 x1 = *reinterpret_cast<const u32x4 *>(Ks + (2 * pr + 1) * RSK + 16 * c8);
+                    const uint32_t xs0[4] = {x0.x, x0.y, x0.z, x0.w}, xs1[4] = {x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t lo = (xs0[e] & 0xffffu) | (xs1[e] << 16);
+                        const uint32_t hi = (xs0[e] >> 16) | (xs1[e] & 0xffff0000u);
+                        *reinterpret_cast<uint32_t *>(buf + L::oKt + (8 * c8 + 2 * e) * RST + 4 * pr) = lo;
+                        *reinterpret_cast<uint32_t *>(buf + L::oKt + (8 * c8 + 2 * e + 1) * RST + 4 * pr) = hi;
+                    }
+                }
+            }
+            prep_sync(pctr, target, lane, pfail);
+
+            // ---- step 3: T_bb = (I + A_bb)^{-1} by forward substitution (wave = block,
+            // lane = column), stored as T_bb - I; four partial sums per row
+            if (lane < 16) {
+                const float *nb = diag + pw * 256;
+                const int cidx = lane;
+                float t[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+                    for (int j4 = 0; j4 < (i + 3) / 4; ++j4) {
+                        const f32x4 av = *reinterpret_cast<const f32x4 *>(nb + i * 16 + 4 * j4);
+                        if (4 * j4 + 0 < i) s0 += av[0] * t[4 * j4 + 0];
+                        if (4 * j4 + 1 < i) s1 += av[1] * t[4 * j4 + 1];
+                        if (4 * j4 + 2 < i) s2 += av[2] * t[4 * j4 + 2];
+                        if (4 * j4 + 3 < i) s3 += av[3] * t[4 * j4 + 3];
+                    }
+                    t[i] = i < cidx ? 0.f : (i == cidx ? 1.f : (s0 + s1) + (s2 + s3));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    st_e(reinterpret_cast<E *>(buf + L::oT) + pw * 256 + i * 16 + cidx, i == cidx ? 0.f : t[i]);
+            }
+        };
+
+        if (nch > 0) {
+            fetch(0);
+            prep(0);
+        }
+        sync_lds();                                  // chunk 0 prepared
+        for (int64_t c = 0; c < nch; ++c) {
+            if (c + 1 < nch) prep(c + 1);
+            sync_lds();
+        }
+        if (*pfail && lane == 0 && pw == 0) *a.status = kStatusBadInput;
+    }
+}
+
+template <int DK, int DV, int W, class P, bool WITH_O>
+hipError_t launch_t(const ChunkArgs &a, hipStream_t stream)
+{
+    const int64_t nblk = (int64_t)a.n_seqs * a.h_v * (DV / W);
+    if (nblk <= 0) return hipSuccess;
+    if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((gdn_chunk_ws_kernel<DK, DV, W, P, WITH_O>), dim3((unsigned)nblk),
+                       dim3(64 * (W / 16 + NPW)), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chunk_ws(const ChunkArgs &a, int bf16, int d_k, int d_v, bool with_o, hipStream_t s)
+{
+#define GDN_DISPATCH(DK, DV, W, POL)                                                   \
+    return with_o ? launch_t<DK, DV, W, POL, true>(a, s) : launch_t<DK, DV, W, POL, false>(a, s)
+    if (bf16) {
+        if (d_k == 128 && d_v == 128) GDN_DISPATCH(128, 128, 128, PolBF16);
+        if (d_k == 64 && d_v == 64) GDN_DISPATCH(64, 64, 64, PolBF16);
+        if (d_k == 128 && d_v == 64) GDN_DISPATCH(128, 64, 64, PolBF16);
+        if (d_k == 64 && d_v == 128) GDN_DISPATCH(64, 128, 128, PolBF16);
+    } else {
+        if (d_k == 64 && d_v == 64) GDN_DISPATCH(64, 64, 64, PolF32);
+        if (d_k == 64 && d_v == 128) GDN_DISPATCH(64, 128, 64, PolF32);
+    }
+#undef GDN_DISPATCH
+    return hipErrorNotSupported;
+}
+
+}  // namespace gdn

@@ -30,6 +30,10 @@ struct ChunkArgs {
 hipError_t launch_chunk(const ChunkArgs &a, int bf16, int d_k, int d_v, bool with_o,
                         hipStream_t stream);
 
+// Warp-specialised variant: state waves and prep waves on double-buffered LDS.
+hipError_t launch_chunk_ws(const ChunkArgs &a, int bf16, int d_k, int d_v, bool with_o,
+                           hipStream_t stream);
+
 hipError_t launch_relerr(const float *A, const float *B, int64_t n_states, int32_t elems,
                          float *relerr, int32_t *nonfinite, hipStream_t stream);
 
