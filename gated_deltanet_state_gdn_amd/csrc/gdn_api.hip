@@ -60,6 +60,12 @@ int32_t check_desc(const gdn_desc *d, bool replay)
         debug("unsupported head dims for this dtype");
         return GDN_ERR_UNSUPPORTED;
     }
+    // one chunk (64 tokens) of any packed tensor is addressed with 32-bit byte offsets
+    const int64_t row_bytes = (int64_t)(d->h_v > d->h_qk ? d->h_v : d->h_qk) * 128 * 4;
+    if (row_bytes * 64 >= 0x7fffffffLL) {
+        debug("too many heads: a 64-token chunk must span less than 2 GiB");
+        return GDN_ERR_SHAPE;
+    }
     return GDN_OK;
 }
 

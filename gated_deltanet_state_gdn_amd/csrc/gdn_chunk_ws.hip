@@ -9,7 +9,7 @@
 //     G_ij = exp(H_i - H_j) if no reset in (j, i], else 0             (j <= i)
 //     A    = strict_lower(diag(b) (K K^T o G))
 //     (I + A) U = Y,  Y = diag(b) (V - diag(e) K S)                     (UT transform)
-//     O    = scale (diag(e) Q S + lower(Q K^T o G) U)
+//     O    = diag(scale e) Q S + P U,   P = scale lower(Q K^T o G)  (diagonal included)
 //     S   <- e_last S + K^T diag(G_last,.) U
 // which equals the token recurrence exactly in exact arithmetic.  The triangular
 // solve runs as forward substitution over 16-row blocks,
@@ -20,23 +20,31 @@
 //   * state waves (one per 16-column tile of S): the sequential pass over the chunks.
 //     S never leaves their MFMA accumulators; the columns of S evolve independently
 //     because (I - b k k^T) acts on the d_k side only, so they exchange nothing.
+//     The outputs are formed transposed (O^T = S^T Q^T + U^T P^T), which puts four
+//     consecutive d_v entries of one token in a lane: one vector store per 16 tokens.
 //   * four prep waves: everything that does not depend on S, one chunk ahead -- the
 //     chunk's K, Q (and K^T) in LDS, the gate scan, the Gram products forming -A and
 //     P, and the diagonal-block inverses.
 // One workgroup barrier per chunk hands a prepared buffer to the state waves; the
 // prep waves order their own steps with a counter in LDS.
 //
-// Precision (bf16 inputs, fp32 state): q/k/v enter MFMA exactly; the gates, b, the
-// unit diagonal of the solve and the diagonal of P are applied in fp32; S enters Q S
-// as hi + lo bf16 (hi in K S); U enters P U and K^T U as hi + lo; P as hi + lo;
-// A_bj, T_bb - I and Z as bf16.  fp32 inputs use fp32 MFMA throughout.
+// Global memory is read and written through buffer resources rebased at every chunk:
+// 32-bit offsets, no per-element 64-bit address arithmetic, and the hardware range
+// check returns zero for the rows past the end of a sequence's last chunk (and drops
+// stores there).  Zero rows are inert: their g and b are 0, so they neither decay nor
+// write the state.
+//
+// Precision (bf16 inputs, fp32 state): q/k/v enter MFMA exactly; the gates, b and the
+// unit diagonal of the solve are applied in fp32; S enters Q S as hi + lo bf16 (hi in
+// K S); U enters P U and K^T U as hi + lo; P as hi + lo; A_bj, T_bb - I and Z as bf16.
+// fp32 inputs use fp32 MFMA throughout.
 //
 // Matrix-core layout used (16x16 MFMA): lane l supplies row l%16 of A and column
 // l%16 of B; element j of lane group l/16 in A pairs with element j of the same
 // lane group in B; the accumulator holds D[4*(l/16)+i][l%16] in element i.  A
 // fragment whose contraction indices follow the accumulator rows lets a D tile be
-// used directly as a B operand (S in K S and Q S, Z/U in the solve, U in P U and
-// K^T U).
+// used directly as a B operand (S in K S, Z/U in the solve, U in K^T U) and, read
+// the other way, as an A operand (S^T in S^T Q^T, U^T in U^T P^T).
 #include <type_traits>
 
 #include "gdn_common.h"
@@ -45,20 +53,31 @@ namespace gdn {
 namespace {
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __amdgpu_buffer_rsrc_t Rsrc;
 
 constexpr int CH = 64;       // chunk length (tokens)
 constexpr int NPW = 4;       // prep waves per workgroup
 
-__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ uint16_t f2bf(float f) {
     __bf16 h = (__bf16)f;                  // round to nearest even (v_cvt_pk_bf16_f32)
     return __builtin_bit_cast(uint16_t, h);
 }
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+// Two floats to a bf16 pair (round to nearest even), the first in the low half.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ float lo_f(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float hi_f(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+// {hi, lo} with hi = bf16(x), lo = bf16(x - hi) for a pair: hi + lo carries 16
+// significant bits.
+__device__ __forceinline__ u32x2 split2(float a, float b) {
+    const uint32_t hi = pk_bf16(a, b);
+    return u32x2{hi, pk_bf16(a - lo_f(hi), b - hi_f(hi))};
 }
 
 // ---------------------------------------------------------------- policies
@@ -84,6 +103,29 @@ __device__ __forceinline__ f32x4 mma(f32x4 c, f32x4 a, f32x4 b) {
 }
 __device__ __forceinline__ f32x4 mma(f32x4 c, bf16x8 a, bf16x8 b) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- global memory
+// Untyped buffer over [base, base + bytes): loads past the end return 0 and stores past
+// it are dropped.
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, int64_t bytes) {
+    const int32_t n = bytes <= 0 ? 0 : (int32_t)(bytes < 0x7fffffffLL ? bytes : 0x7fffffffLL);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+// One element of q/k/v in a register, kept in its storage width until it is used (a
+// widening right after the load would make the loop wait for it early).
+template <class P> struct Raw {
+    typedef typename std::conditional<P::kBF16, uint16_t, uint32_t>::type T;
+};
+template <class P>
+__device__ __forceinline__ typename Raw<P>::T load_e(Rsrc r, uint32_t off) {
+    if constexpr (P::kBF16) return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+template <class P>
+__device__ __forceinline__ float v_at(typename Raw<P>::T v) {
+    if constexpr (P::kBF16) return __uint_as_float((uint32_t)v << 16);
+    else return __uint_as_float(v);
 }
 
 // ---------------------------------------------------------------- LDS layouts
@@ -124,7 +166,7 @@ __device__ __forceinline__ u32x2 tile_half(const uint16_t *T, int tile, int lane
     if (tile < 0) return u32x2{0u, 0u};
     return *reinterpret_cast<const u32x2 *>(T + tile * 256 + (lane & 15) * 16 + 4 * (lane >> 4));
 }
-// bf16 A fragment for k-block kb of tile row ti: tiles (ti, 2kb) and (ti, 2kb + 1);
+// bf16 fragment for k-block kb of tile row ti: tiles (ti, 2kb) and (ti, 2kb + 1);
 // ta, tb are tile indices or -1 for a zero half.
 __device__ __forceinline__ bf16x8 frag_tiles(const uint16_t *T, int ta, int tb, int lane) {
     const u32x2 a = tile_half(T, ta, lane), b = tile_half(T, tb, lane);
@@ -135,40 +177,23 @@ __device__ __forceinline__ f32x4 frag_tile(const float *T, int tile, int lane) {
     return *reinterpret_cast<const f32x4 *>(T + tile * 256 + (lane & 15) * 16 + 4 * (lane >> 4));
 }
 
-// ---------------------------------------------------------------- B operands
+// ---------------------------------------------------------------- register operands
+// Two accumulator tiles (16 contraction rows each) as one bf16 operand.
 __device__ __forceinline__ bf16x8 bfrag_hi(const f32x4 &t0, const f32x4 &t1) {
-    const u32x4 u = {pack2(t0[0], t0[1]), pack2(t0[2], t0[3]), pack2(t1[0], t1[1]),
-                     pack2(t1[2], t1[3])};
+    const u32x4 u = {pk_bf16(t0[0], t0[1]), pk_bf16(t0[2], t0[3]), pk_bf16(t1[0], t1[1]),
+                     pk_bf16(t1[2], t1[3])};
     return __builtin_bit_cast(bf16x8, u);
 }
 __device__ __forceinline__ void bfrag_split(const f32x4 &t0, const f32x4 &t1, bf16x8 &hi,
                                             bf16x8 &lo) {
-    float h[8], r[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        h[i] = bf2f(f2bf(t0[i]));
-        h[4 + i] = bf2f(f2bf(t1[i]));
-        r[i] = t0[i] - h[i];
-        r[4 + i] = t1[i] - h[4 + i];
-    }
-    const u32x4 uh = {pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
-    const u32x4 ul = {pack2(r[0], r[1]), pack2(r[2], r[3]), pack2(r[4], r[5]), pack2(r[6], r[7])};
-    hi = __builtin_bit_cast(bf16x8, uh);
-    lo = __builtin_bit_cast(bf16x8, ul);
+    const u32x2 a = split2(t0[0], t0[1]), b = split2(t0[2], t0[3]);
+    const u32x2 c = split2(t1[0], t1[1]), d = split2(t1[2], t1[3]);
+    hi = __builtin_bit_cast(bf16x8, u32x4{a.x, b.x, c.x, d.x});
+    lo = __builtin_bit_cast(bf16x8, u32x4{a.y, b.y, c.y, d.y});
 }
 
 __device__ __forceinline__ void st_e(float *p, float x) { *p = x; }
 __device__ __forceinline__ void st_e(uint16_t *p, float x) { *p = f2bf(x); }
-
-// V held in registers between its load and Y, one element per register.
-template <class P> struct VHold {
-    typedef typename std::conditional<P::kBF16, uint32_t, float>::type T;
-};
-template <class P>
-__device__ __forceinline__ float v_at(typename VHold<P>::T v) {
-    if constexpr (P::kBF16) return __uint_as_float(v << 16);
-    else return v;
-}
 
 // Lower-triangular 16x16 tile list of a 64x64 product (ti >= tj).
 __device__ __forceinline__ void tri_tile(int idx, int &ti, int &tj) {
@@ -214,7 +239,7 @@ struct Lds {
     static constexpr int RSK = RBK + 16;                       // padded K / Q row stride
     static constexpr int RST = CH * 2 + 16;                    // padded K^T row stride (bf16)
     static constexpr int TILE = 256 * (int)sizeof(E);          // one 16x16 tile
-    static constexpr int oGate = 0;                            // H, e, b, G_last, Pd, rho
+    static constexpr int oGate = 0;                            // H, e, b, G_last, scale e, rho
     static constexpr int oK = 6 * CH * 4;
     static constexpr int oQ = oK + CH * RSK;
     static constexpr int oKt = oQ + (WITH_O ? CH * RSK : 0);
@@ -228,14 +253,23 @@ struct Lds {
     static constexpr int bytes = oMisc + 64;
 };
 
-template <class P, int KBK, int RSK>
-__device__ __forceinline__ f32x4 gram16(const char *Am, const char *Bm, int ti, int tj, int lane) {
-    f32x4 gr = {0.f, 0.f, 0.f, 0.f};
+// Gram tile (ti, tj) of one chunk, computed as (K_tj K_ti^T) and (K_tj Q_ti^T) so that
+// element i of lane l is
+//     kk[i] = k_{16 tj + 4 (l/16) + i} . k_{16 ti + l%16},
+//     qk[i] = k_{16 tj + 4 (l/16) + i} . q_{16 ti + l%16},
+// i.e. entry (16 ti + l%16, 16 tj + 4 (l/16) + i) of K K^T and of Q K^T: four
+// consecutive columns of one row per lane, stored with one vector write.
+template <class P, int KBK, int RSK, bool WITH_O>
+__device__ __forceinline__ void gram_t(const char *Ks, const char *Qs, int ti, int tj, int lane,
+                                       f32x4 &kk, f32x4 &qk) {
+    kk = f32x4{0.f, 0.f, 0.f, 0.f};
+    qk = kk;
 #pragma unroll
-    for (int kb = 0; kb < KBK; ++kb)
-        gr = mma(gr, frag_rm<RSK>(Am, 16 * ti, kb, lane, typename P::E()),
-                 frag_rm<RSK>(Bm, 16 * tj, kb, lane, typename P::E()));
-    return gr;
+    for (int kb = 0; kb < KBK; ++kb) {
+        const auto kj = frag_rm<RSK>(Ks, 16 * tj, kb, lane, typename P::E());
+        kk = mma(kk, kj, frag_rm<RSK>(Ks, 16 * ti, kb, lane, typename P::E()));
+        if constexpr (WITH_O) qk = mma(qk, kj, frag_rm<RSK>(Qs, 16 * ti, kb, lane, typename P::E()));
+    }
 }
 
 // ---------------------------------------------------------------- kernel
@@ -260,7 +294,8 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
     int *pctr = reinterpret_cast<int *>(smem + L::oMisc + 8);
     int *pfail = reinterpret_cast<int *>(smem + L::oMisc + 12);
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane0 = tid & 63;
+    const int tid = threadIdx.x, lane0 = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int lane = lane0, lr = lane & 15, lg = lane >> 4;
     const bool is_state = wave < NSW;
 
@@ -342,22 +377,26 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                 S[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
-        // V rows of a chunk in accumulator layout; rows past the chunk end read the
-        // last valid row (finite; their b is 0, so they never contribute)
-        typename VHold<P>::T vreg[4][4];
+        // V rows of a chunk in accumulator layout (rows past the window read as 0; a
+        // chunk past the window gets an empty buffer and touches no memory)
+        const uint32_t vrow = (uint32_t)a.h_v * (uint32_t)(DV * sizeof(E));   // bytes per token
+        typename Raw<P>::T vreg[4][4];
         auto fetch_v = [&](int64_t cc) {
-            const int ln = (int)((rn - cc) < CH ? (rn - cc) : CH);
-            const int64_t tb = wbeg + cc;
+            int lane = lane0;
+            asm volatile("" : "+v"(lane));
+            const int64_t ln = (rn - cc) < CH ? (rn - cc) : CH;
+            const Rsrc rs = make_rsrc(vg + ((wbeg + cc) * a.h_v + h) * (int64_t)DV + col0,
+                                      ln * (int64_t)vrow);
+            const uint32_t vo = (uint32_t)(4 * (lane >> 4)) * vrow + (uint32_t)(lane & 15) * (uint32_t)sizeof(E);
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = min(16 * tt + 4 * lg + i, ln - 1);
-                    const E x = vg[((tb + row) * a.h_v + h) * DV + col0 + lr];
-                    if constexpr (P::kBF16) vreg[tt][i] = (uint32_t)x;
-                    else vreg[tt][i] = x;
-                }
+                for (int i = 0; i < 4; ++i)
+                    vreg[tt][i] = load_e<P>(rs, vo + (uint32_t)(16 * tt + i) * vrow);
         };
+        // the initial state is in registers before the loop, so no wait for it is left
+        // inside the loop (vmcnt(0) only; expcnt and lgkmcnt at their maxima)
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         if (nch > 0) fetch_v(0);
         sync_lds();                                  // chunk 0 prepared
 
@@ -373,14 +412,14 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             const char *Ks = buf + L::oK;
             const char *Qs = buf + L::oQ;
             const float *gH = reinterpret_cast<const float *>(buf + L::oGate);
-            const float *gE = gH + CH, *gB = gE + CH, *gL = gB + CH, *gPd = gL + CH;
+            const float *gE = gH + CH, *gB = gE + CH, *gL = gB + CH, *gEs = gL + CH;
 
-            // X = K S (S as hi bf16) and Q S (S as hi + lo), k-block by k-block
-            f32x4 X[4], QS[4];
+            // X = K S (S as hi bf16) and (Q S)^T = S^T Q^T (S as hi + lo), by k-block
+            f32x4 X[4], OT[4];
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 X[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                QS[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                OT[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
             for (int kb = 0; kb < KBK; ++kb) {
@@ -392,8 +431,8 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                     X[tt] = mma(X[tt], frag_rm<RSK>(Ks, 16 * tt, kb, lane, E()), sh);
                     if constexpr (WITH_O) {
                         const Frag qf = frag_rm<RSK>(Qs, 16 * tt, kb, lane, E());
-                        QS[tt] = mma(QS[tt], qf, sh);
-                        if constexpr (P::kBF16) QS[tt] = mma(QS[tt], qf, sl);
+                        OT[tt] = mma(OT[tt], sh, qf);
+                        if constexpr (P::kBF16) OT[tt] = mma(OT[tt], sl, qf);
                     }
                 }
             }
@@ -405,7 +444,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
 #pragma unroll
                 for (int i = 0; i < 4; ++i) X[tt][i] = br[i] * (v_at<P>(vreg[tt][i]) - er[i] * X[tt][i]);
             }
-            if (c + 1 < nch) fetch_v(c0 + CH);       // lands while this chunk is processed
+            fetch_v(c0 + CH);   // lands while this chunk is processed (past the end: no access)
 
             // (I + A) U = Y by 16-row block forward substitution
             f32x4 U[4];
@@ -440,7 +479,8 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                 }
             }
 
-            // O = e (Q S) + Pd U + P_off U   (QS registers become O), stored from registers
+            // O^T = (S^T Q^T) diag(scale e) + U^T P^T; lane: token 16 tt + l%16, d_v
+            // columns col0 + 4 (l/16) + i
             if constexpr (WITH_O) {
                 Frag uh[KBT], ul[KBT];
 #pragma unroll
@@ -452,10 +492,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                 const E *Pl = reinterpret_cast<const E *>(buf + L::oPl);
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
-                    const f32x4 er = *reinterpret_cast<const f32x4 *>(gE + 16 * tt + 4 * lg);
-                    const f32x4 pd = *reinterpret_cast<const f32x4 *>(gPd + 16 * tt + 4 * lg);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) QS[tt][i] = er[i] * QS[tt][i] + pd[i] * U[tt][i];
+                    OT[tt] *= gEs[16 * tt + lr];
 #pragma unroll
                     for (int kb = 0; kb < KBT; ++kb) {
                         if (kb * P::KB < 16 * tt + 16) {
@@ -463,29 +500,37 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                                 const int ta = tri_index(tt, 2 * kb);
                                 const int tb = (2 * kb + 1 <= tt) ? tri_index(tt, 2 * kb + 1) : -1;
                                 const Frag ph = frag_tiles(Ph, ta, tb, lane);
-                                QS[tt] = mma(QS[tt], ph, uh[kb]);
-                                QS[tt] = mma(QS[tt], ph, ul[kb]);
-                                QS[tt] = mma(QS[tt], frag_tiles(Pl, ta, tb, lane), uh[kb]);
+                                OT[tt] = mma(OT[tt], uh[kb], ph);
+                                OT[tt] = mma(OT[tt], ul[kb], ph);
+                                OT[tt] = mma(OT[tt], uh[kb], frag_tiles(Pl, ta, tb, lane));
                             } else {
-                                QS[tt] = mma(QS[tt], frag_tile(Ph, tri_index(tt, kb), lane), uh[kb]);
+                                OT[tt] = mma(OT[tt], uh[kb], frag_tile(Ph, tri_index(tt, kb), lane));
                             }
                         }
                     }
                 }
                 if (a.o_out) {
-                    const int64_t obase = replay ? orow0 + c0 : wbeg + c0;
+                    // rows past the window end fall outside the buffer and are dropped
+                    const int64_t orow_first = replay ? orow0 + c0 : wbeg + c0;
+                    const bool f32o = !P::kBF16 || a.o_f32;
+                    const uint32_t osz = f32o ? 4u : 2u;
+                    const uint32_t orow = (uint32_t)a.h_v * (uint32_t)DV * osz;
+                    const Rsrc rs = make_rsrc(reinterpret_cast<const char *>(a.o_out) +
+                                                  ((orow_first * a.h_v + h) * DV + col0) * (int64_t)osz,
+                                              (int64_t)len * orow);
+                    const uint32_t ob = (uint32_t)lr * orow + (uint32_t)(4 * lg) * osz;
+                    if (f32o) {
 #pragma unroll
-                    for (int tt = 0; tt < 4; ++tt)
+                        for (int tt = 0; tt < 4; ++tt)
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, OT[tt]), rs,
+                                                                   ob + (uint32_t)(16 * tt) * orow, 0, 0);
+                    } else {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int rr = 16 * tt + 4 * lg + i;
-                            if (rr < len) {
-                                const int64_t off = ((obase + rr) * a.h_v + h) * DV + col0 + lr;
-                                const float ov = a.scale * QS[tt][i];
-                                if (a.o_f32) reinterpret_cast<float *>(a.o_out)[off] = ov;
-                                else st_e(reinterpret_cast<E *>(a.o_out) + off, ov);
-                            }
+                        for (int tt = 0; tt < 4; ++tt) {
+                            const u32x2 pk = {pk_bf16(OT[tt][0], OT[tt][1]), pk_bf16(OT[tt][2], OT[tt][3])};
+                            __builtin_amdgcn_raw_buffer_store_b64(pk, rs, ob + (uint32_t)(16 * tt) * orow, 0, 0);
                         }
+                    }
                 }
             }
 
@@ -533,33 +578,38 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         // =====================================================================
         // prep waves: chunk c + 1's operands while the state waves process chunk c
         const int pw = wave - NSW;                 // 0..NPW-1
-        const int ptid = tid - 64 * NSW;           // 0..255
         int target = 0;
-        constexpr int NVK = CH * RBK / 16;         // 16-byte vectors of a K (or Q) chunk
-        constexpr int NVT = NVK / (64 * NPW);      // per prep thread
-        constexpr int NCK = RBK / 16;              // vectors per row
-        static_assert(NVK % (64 * NPW) == 0, "vector map");
+        constexpr int NCK = RBK / 16;              // 16-byte vectors per K (or Q) row
+        constexpr int RPJ = 64 * NPW / NCK;        // rows per load round
+        constexpr int NVT = CH / RPJ;              // load rounds per chunk
+        static_assert((64 * NPW) % NCK == 0 && CH % RPJ == 0, "vector map");
+        const uint32_t krow = (uint32_t)a.h_qk * (uint32_t)RBK;    // bytes per token
+        const uint32_t grow = (uint32_t)a.h_v * 4u;
         u32x4 kpf[NVT], qpf[NVT];
-        float gpf = 0.f, bpf = 0.f;
-        bool gok = false;
-        // rows past the chunk end load the last valid row: finite, and inert because
-        // their g and beta are set to 0 (alpha = 1, no write)
+        uint32_t gpf = 0, bpf = 0;
+        // the chunk starting at token cc of the window into registers (rows past the
+        // window read as 0: g = b = 0 there)
         auto fetch = [&](int64_t cc) {
-            const int ln = (int)((rn - cc) < CH ? (rn - cc) : CH);
-            const int64_t tb = wbeg + cc;
+            int lane = lane0;
+            asm volatile("" : "+v"(lane));
+            const int pt = 64 * pw + lane;
+            const int64_t ln = (rn - cc) < CH ? (rn - cc) : CH;
+            const int64_t t0 = wbeg + cc;
+            const int64_t koff = (t0 * a.h_qk + hk) * (int64_t)DK;
+            const Rsrc rk = make_rsrc(kg + koff, ln * (int64_t)krow);
+            const Rsrc rq = make_rsrc(qg + koff, ln * (int64_t)krow);
+            const uint32_t vo = (uint32_t)(pt / NCK) * krow + (uint32_t)(pt % NCK) * 16u;
 #pragma unroll
             for (int j = 0; j < NVT; ++j) {
-                const int u = ptid + 64 * NPW * j;
-                const int row = min(u / NCK, ln - 1);
-                const int64_t off = ((tb + row) * a.h_qk + hk) * DK + (int64_t)(u % NCK) * (16 / sizeof(E));
-                kpf[j] = *reinterpret_cast<const u32x4 *>(kg + off);
-                if (WITH_O) qpf[j] = *reinterpret_cast<const u32x4 *>(qg + off);
+                kpf[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo + (uint32_t)(RPJ * j) * krow, 0, 0);
+                if (WITH_O)
+                    qpf[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, vo + (uint32_t)(RPJ * j) * krow, 0, 0);
             }
             if (pw == 0) {
-                const int64_t off = (tb + min(lane, ln - 1)) * a.h_v + h;
-                gpf = a.g[off];
-                bpf = a.beta[off];
-                gok = lane < ln;
+                const Rsrc rg = make_rsrc(a.g + t0 * a.h_v + h, ln * (int64_t)grow);
+                const Rsrc rb = make_rsrc(a.beta + t0 * a.h_v + h, ln * (int64_t)grow);
+                gpf = __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)lane * grow, 0, 0);
+                bpf = __builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)lane * grow, 0, 0);
             }
         };
 
@@ -567,21 +617,22 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             int lane = lane0;
             asm volatile("" : "+v"(lane));
             const int lr = lane & 15, lg = lane >> 4;
+            const int pt = 64 * pw + lane;
             char *buf = smem + (cc & 1) * L::BUF;
             char *Ks = buf + L::oK;
             char *Qs = buf + L::oQ;
             float *gH = reinterpret_cast<float *>(buf + L::oGate);
-            float *gE = gH + CH, *gB = gE + CH, *gL = gB + CH, *gPd = gL + CH;
-            int *gR = reinterpret_cast<int *>(gPd + CH);
+            float *gE = gH + CH, *gB = gE + CH, *gL = gB + CH, *gEs = gL + CH;
+            int *gR = reinterpret_cast<int *>(gEs + CH);
             // ---- step 1: K, Q into LDS; gate scan; fetch the chunk after
 #pragma unroll
             for (int j = 0; j < NVT; ++j) {
-                const int u = ptid + 64 * NPW * j;
-                *reinterpret_cast<u32x4 *>(Ks + (u / NCK) * RSK + (u % NCK) * 16) = kpf[j];
-                if (WITH_O) *reinterpret_cast<u32x4 *>(Qs + (u / NCK) * RSK + (u % NCK) * 16) = qpf[j];
+                const int off = (pt / NCK + RPJ * j) * RSK + (pt % NCK) * 16;
+                *reinterpret_cast<u32x4 *>(Ks + off) = kpf[j];
+                if (WITH_O) *reinterpret_cast<u32x4 *>(Qs + off) = qpf[j];
             }
             if (pw == 0) {
-                const float gv = gok ? gpf : 0.f, bv = gok ? bpf : 0.f;
+                const float gv = __uint_as_float(gpf), bv = __uint_as_float(bpf);
                 // reset-aware inclusive scan: H = sum of g since the last alpha = 0 token
                 const bool reset = gv == -__builtin_inff();
                 float hv = reset ? 0.f : gv;
@@ -600,82 +651,88 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                 }
                 const float hl = __shfl(hv, 63);
                 const int rl = __shfl(rho, 63);
+                const float ev = rho < 0 ? __expf(hv) : 0.f;
                 gH[lane] = hv;
-                gE[lane] = rho < 0 ? __expf(hv) : 0.f;
+                gE[lane] = ev;
+                gEs[lane] = a.scale * ev;
                 gB[lane] = bv;
                 gR[lane] = rho;
                 gL[lane] = rl <= lane ? __expf(hl - hv) : 0.f;
             }
-            if (cc + 1 < nch) fetch((cc + 1) * CH);
+            fetch((cc + 1) * CH);   // past the window: an empty buffer, no access
             prep_sync(pctr, target, lane, pfail);
 
             // ---- step 2: Gram tiles -> -A (tiles, and fp32 diagonal blocks for the
-            // inverses), P (hi + lo) and its diagonal; K^T
-            constexpr int NG = WITH_O ? 20 : 10;
+            // inverses) and P = scale lower(Q K^T o G) (hi + lo); K^T
+            // (tile indices are compile-time: every LDS address folds into an offset)
 #pragma unroll
-            for (int j = 0; j < (NG + NPW - 1) / NPW; ++j) {
-                const int idx = pw + NPW * j;
-                if (idx < NG) {
-                    const bool isP = idx >= 10;
+            for (int idx = 0; idx < 10; ++idx) {
+                if (idx % NPW == pw) {
                     int ti, tj;
-                    tri_tile(isP ? idx - 10 : idx, ti, tj);
-                    const f32x4 gr = gram16<P, KBK, RSK>(isP ? Qs : Ks, Ks, ti, tj, lane);
-                    const int c = 16 * tj + lr;
-                    const float hc = gH[c];
-                    const f32x4 hr = *reinterpret_cast<const f32x4 *>(gH + 16 * ti + 4 * lg);
-                    const f32x4 br = *reinterpret_cast<const f32x4 *>(gB + 16 * ti + 4 * lg);
-                    const int4 rr4 = *reinterpret_cast<const int4 *>(gR + 16 * ti + 4 * lg);
-                    const int rrs[4] = {rr4.x, rr4.y, rr4.z, rr4.w};
-                    const int tile = tri_index(ti, tj);
+                    tri_tile(idx, ti, tj);
+                    f32x4 kk, qk;
+                    gram_t<P, KBK, RSK, WITH_O>(Ks, Qs, ti, tj, lane, kk, qk);
+                    const int rr = 16 * ti + lr;              // row of this lane
+                    const float hr = gH[rr], br = gB[rr];
+                    const int rho = gR[rr];
+                    const f32x4 hc = *reinterpret_cast<const f32x4 *>(gH + 16 * tj + 4 * lg);
+                    f32x4 av, pv;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int rr = 16 * ti + 4 * lg + i;
-                        const float gam = (c < rr && rrs[i] <= c) ? __expf(hr[i] - hc) : 0.f;
-                        const int e = tile * 256 + (4 * lg + i) * 16 + lr;
-                        if (!isP) {
-                            const float na = -br[i] * gam * gr[i];
-                            st_e(reinterpret_cast<E *>(buf + L::oA) + e, na);
-                            if (ti == tj) diag[ti * 256 + (4 * lg + i) * 16 + lr] = na;
-                        } else if constexpr (WITH_O) {
-                            const float pv = gam * gr[i];
-                            if constexpr (P::kBF16) {
-                                const uint16_t hb = f2bf(pv);
-                                reinterpret_cast<uint16_t *>(buf + L::oPh)[e] = hb;
-                                reinterpret_cast<uint16_t *>(buf + L::oPl)[e] = f2bf(pv - bf2f(hb));
-                            } else {
-                                reinterpret_cast<float *>(buf + L::oPh)[e] = pv;
-                            }
-                            if (c == rr) gPd[rr] = gr[i];
+                    for (int e = 0; e < 4; ++e) {
+                        const int c = 16 * tj + 4 * lg + e;
+                        const float gam = (c <= rr && rho <= c) ? __expf(hr - hc[e]) : 0.f;
+                        av[e] = c < rr ? -br * gam * kk[e] : 0.f;
+                        pv[e] = a.scale * gam * qk[e];
+                    }
+                    const int eo = tri_index(ti, tj) * 256 + lr * 16 + 4 * lg;
+                    if (ti == tj) *reinterpret_cast<f32x4 *>(diag + ti * 256 + lr * 16 + 4 * lg) = av;
+                    if constexpr (P::kBF16) {
+                        *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(buf + L::oA) + eo) =
+                            u32x2{pk_bf16(av[0], av[1]), pk_bf16(av[2], av[3])};
+                        if constexpr (WITH_O) {
+                            const u32x2 p01 = split2(pv[0], pv[1]), p23 = split2(pv[2], pv[3]);
+                            *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(buf + L::oPh) + eo) =
+                                u32x2{p01.x, p23.x};
+                            *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(buf + L::oPl) + eo) =
+                                u32x2{p01.y, p23.y};
                         }
+                    } else {
+                        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(buf + L::oA) + eo) = av;
+                        if constexpr (WITH_O)
+                            *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(buf + L::oPh) + eo) = pv;
                     }
                 }
             }
             if constexpr (P::kBF16) {
-                // K^T[dk][t] as packed token pairs: thread -> (token pair, 8-column block)
-                constexpr int NCB8 = DK / 8;
+                // K^T[dk][t] as packed token pairs, by the two waves with fewer Gram
+                // tiles: thread -> (token pair, 8-column block)
+                constexpr int NU = 32 * (DK / 8);
+                static_assert(NU % 128 == 0, "K^T map");
+                if (pw >= 2) {
 #pragma unroll
-                for (int j = 0; j < (32 * NCB8) / (64 * NPW); ++j) {
-                    const int u = ptid + 64 * NPW * j;
-                    const int pr = u & 31, c8 = u >> 5;
-                    const u32x4 x0 = *reinterpret_cast<const u32x4 *>(Ks + (2 * pr) * RSK + 16 * c8);
-                    const u32x4 x1 = *reinterpret_cast<const u32x4 *>(Ks + (2 * pr + 1) * RSK + 16 * c8);
-                    const uint32_t xs0[4] = {x0.x, x0.y, x0.z, x0.w}, xs1[4] = {x1.x, x1.y, x1.z, x1.w};
+                    for (int j = 0; j < NU / 128; ++j) {
+                        const int u = (pt - 128) + 128 * j;
+                        const int pr = u & 31, c8 = u >> 5;
+                        const u32x4 x0 = *reinterpret_cast<const u32x4 *>(Ks + (2 * pr) * RSK + 16 * c8);
+                        const u32x4 x1 = *reinterpret_cast<const u32x4 *>(Ks + (2 * pr + 1) * RSK + 16 * c8);
+                        const uint32_t xs0[4] = {x0.x, x0.y, x0.z, x0.w}, xs1[4] = {x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t lo = (xs0[e] & 0xffffu) | (xs1[e] << 16);
-                        const uint32_t hi = (xs0[e] >> 16) | (xs1[e] & 0xffff0000u);
-                        *reinterpret_cast<uint32_t *>(buf + L::oKt + (8 * c8 + 2 * e) * RST + 4 * pr) = lo;
-                        *reinterpret_cast<uint32_t *>(buf + L::oKt + (8 * c8 + 2 * e + 1) * RST + 4 * pr) = hi;
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t lo = (xs0[e] & 0xffffu) | (xs1[e] << 16);
+                            const uint32_t hi = (xs0[e] >> 16) | (xs1[e] & 0xffff0000u);
+                            *reinterpret_cast<uint32_t *>(buf + L::oKt + (8 * c8 + 2 * e) * RST + 4 * pr) = lo;
+                            *reinterpret_cast<uint32_t *>(buf + L::oKt + (8 * c8 + 2 * e + 1) * RST + 4 * pr) = hi;
+                        }
                     }
                 }
             }
             prep_sync(pctr, target, lane, pfail);
 
-            // ---- step 3: T_bb = (I + A_bb)^{-1} by forward substitution (wave = block,
-            // lane = column), stored as T_bb - I; four partial sums per row
-            if (lane < 16) {
-                const float *nb = diag + pw * 256;
-                const int cidx = lane;
+            // ---- step 3: T_bb = (I + A_bb)^{-1} by forward substitution, one wave:
+            // lane = (block l/16, column l%16); stored as T_bb - I; four partial sums
+            if (pw == 0) {
+                const int blk = lane >> 4, cidx = lane & 15;
+                const float *nb = diag + blk * 256;
                 float t[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -691,9 +748,9 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                     t[i] = i < cidx ? 0.f : (i == cidx ? 1.f : (s0 + s1) + (s2 + s3));
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                E *Tt = reinterpret_cast<E *>(buf + L::oT) + blk * 256 + cidx;
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    st_e(reinterpret_cast<E *>(buf + L::oT) + pw * 256 + i * 16 + cidx, i == cidx ? 0.f : t[i]);
+                for (int i = 0; i < 16; ++i) st_e(Tt + i * 16, i == cidx ? 0.f : t[i]);
             }
         };
 
