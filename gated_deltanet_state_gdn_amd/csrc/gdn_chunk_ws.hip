@@ -129,48 +129,57 @@ __device__ __forceinline__ float v_at(typename Raw<P>::T v) {
 }
 
 // ---------------------------------------------------------------- LDS layouts
-// Row-major matrices with padded rows (RS bytes per row, 16 more than the data) so
-// that the 16 rows a fragment reads land on different banks; every fragment of a
-// matrix then shares one lane-dependent base address plus a constant offset.
-// A-operand fragment (or B = M^T): lane l gives row r0 + l%16 and the contraction
-// indices {4*(l/16) + i} (+16 for bf16) of k-block kb.
-template <int RS>
-__device__ __forceinline__ bf16x8 frag_rm(const char *M, int r0, int kb, int lane, uint16_t) {
-    const char *p = M + (r0 + (lane & 15)) * RS + kb * 64 + 8 * (lane >> 4);
-    const u32x2 a = *reinterpret_cast<const u32x2 *>(p);
-    const u32x2 b = *reinterpret_cast<const u32x2 *>(p + 32);
-    const u32x4 u = {a.x, a.y, b.x, b.y};
-    return __builtin_bit_cast(bf16x8, u);
+// Operand matrices (K, Q, K^T) are row-major with RB-byte rows of 16-byte chunks and no
+// padding: logical chunk c of row r sits at chunk c ^ swz(r), which spreads the 16 rows
+// that one fragment read touches over all banks (16-byte reads run at full rate).
+// bf16 columns are permuted inside every 32-column block so that one chunk holds a whole
+// fragment: logical chunk 4 kb + g carries columns 32 kb + {4g..4g+3, 16+4g..16+4g+3},
+// the contraction indices that pair with accumulator rows 4g + i of two 16-row tiles.
+// fp32 keeps the natural order (logical chunk 4 kb + g = columns 16 kb + 4g .. 4g+3).
+template <int RB>
+__device__ __forceinline__ int swz(int r) { return RB == 256 ? (r & 15) : ((r >> 1) & 7); }
+template <int RB>
+__device__ __forceinline__ int chunk_at(int r, int c) { return r * RB + 16 * (c ^ swz<RB>(r)); }
+
+// A-operand fragment (or B = M^T): lane l gives row r0 + l%16 and logical chunk
+// 4 kb + l/16 (r0 a multiple of 16).
+template <int RB, class F>
+__device__ __forceinline__ F frag_sw(const char *M, int r0, int kb, int lane) {
+    return __builtin_bit_cast(
+        F, *reinterpret_cast<const u32x4 *>(M + chunk_at<RB>(r0 + (lane & 15), 4 * kb + (lane >> 4))));
 }
-template <int RS>
-__device__ __forceinline__ f32x4 frag_rm(const char *M, int r0, int kb, int lane, float) {
-    return *reinterpret_cast<const f32x4 *>(M + (r0 + (lane & 15)) * RS + kb * 64 + 16 * (lane >> 4));
-}
-// fp32 fragment of M^T for a row-major fp32 matrix whose rows are the contraction
-// index: lane l gives column c0 + l%16, rows kb*16 + 4*(l/16) + i.
-template <int RS>
-__device__ __forceinline__ f32x4 frag_rm_cols(const char *M, int c0, int kb, int lane) {
-    const char *p = M + (kb * 16 + 4 * (lane >> 4)) * RS + 4 * (c0 + (lane & 15));
+// fp32 fragment of M^T (the rows of M are the contraction index): lane l gives column
+// c0 + l%16 and rows 16 kb + 4 (l/16) + i.
+template <int RB>
+__device__ __forceinline__ f32x4 frag_cols_f32(const char *M, int c0, int kb, int lane) {
+    const int col = c0 + (lane & 15);
     f32x4 f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = *reinterpret_cast<const float *>(p + i * RS);
+    for (int i = 0; i < 4; ++i) {
+        const int row = 16 * kb + 4 * (lane >> 4) + i;
+        f[i] = *reinterpret_cast<const float *>(M + chunk_at<RB>(row, col >> 2) + 4 * (col & 3));
+    }
     return f;
 }
 
-// 16x16 tiles, row-major (32-byte rows in bf16, 64-byte rows in fp32).  Lower-triangular
-// tile (ti >= tj) of a 64x64 matrix lives at index ti*(ti+1)/2 + tj.
-__device__ __forceinline__ int tri_index(int ti, int tj) { return ti * (ti + 1) / 2 + tj; }
-
-// Half fragment (4 contraction indices) from a tile, or zeros when tile < 0.
-__device__ __forceinline__ u32x2 tile_half(const uint16_t *T, int tile, int lane) {
-    if (tile < 0) return u32x2{0u, 0u};
-    return *reinterpret_cast<const u32x2 *>(T + tile * 256 + (lane & 15) * 16 + 4 * (lane >> 4));
+// bf16 tile pairs: the 16 x 32 block (16-row block ti, 32-column block kb) of a 64x64
+// lower-triangular matrix, rows of 64 bytes; logical chunk g of row r holds columns
+// 4g..4g+3 of tile (ti, 2kb) then of tile (ti, 2kb+1), stored at chunk g ^ ((r >> 2) & 3).
+// Pair index of (ti, kb), kb <= ti/2:  0:(0,0) 1:(1,0) 2:(2,0) 3:(2,1) 4:(3,0) 5:(3,1).
+__device__ __forceinline__ int dt_index(int ti, int kb) { return ti < 2 ? ti : 2 * ti - 2 + kb; }
+__device__ __forceinline__ int dt_at(int r, int g) { return r * 64 + 16 * (g ^ ((r >> 2) & 3)); }
+__device__ __forceinline__ bf16x8 frag_dt(const char *T, int pair, int lane) {
+    return __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const u32x4 *>(T + pair * 1024 + dt_at(lane & 15, lane >> 4)));
 }
-// bf16 fragment for k-block kb of tile row ti: tiles (ti, 2kb) and (ti, 2kb + 1);
-// ta, tb are tile indices or -1 for a zero half.
-__device__ __forceinline__ bf16x8 frag_tiles(const uint16_t *T, int ta, int tb, int lane) {
-    const u32x2 a = tile_half(T, ta, lane), b = tile_half(T, tb, lane);
-    const u32x4 u = {a.x, a.y, b.x, b.y};
+
+// 16x16 tiles, row-major (32-byte rows in bf16, 64-byte rows in fp32): T_bb - I, and for
+// fp32 inputs also -A and P; lower tile (ti, tj) of a 64x64 matrix at ti*(ti+1)/2 + tj.
+__device__ __forceinline__ int tri_index(int ti, int tj) { return ti * (ti + 1) / 2 + tj; }
+// bf16 fragment with one half (4 contraction indices) from a tile and the other zero.
+__device__ __forceinline__ bf16x8 frag_half(const uint16_t *T, int tile, bool upper, int lane) {
+    const u32x2 a = *reinterpret_cast<const u32x2 *>(T + tile * 256 + (lane & 15) * 16 + 4 * (lane >> 4));
+    const u32x4 u = upper ? u32x4{0u, 0u, a.x, a.y} : u32x4{a.x, a.y, 0u, 0u};
     return __builtin_bit_cast(bf16x8, u);
 }
 __device__ __forceinline__ f32x4 frag_tile(const float *T, int tile, int lane) {
@@ -236,20 +245,22 @@ template <int DK, class P, bool WITH_O>
 struct Lds {
     typedef typename P::E E;
     static constexpr int RBK = DK * (int)sizeof(E);          // K / Q row bytes
-    static constexpr int RSK = RBK + 16;                       // padded K / Q row stride
-    static constexpr int RST = CH * 2 + 16;                    // padded K^T row stride (bf16)
+    static constexpr int RBT = CH * 2;                         // K^T row bytes (bf16)
     static constexpr int TILE = 256 * (int)sizeof(E);          // one 16x16 tile
+    static constexpr int NTA = P::kBF16 ? 6 : 10;              // tile pairs (bf16) / tiles (fp32)
+    static constexpr int UNIT = P::kBF16 ? 1024 : TILE;
     static constexpr int oGate = 0;                            // H, e, b, G_last, scale e, rho
     static constexpr int oK = 6 * CH * 4;
-    static constexpr int oQ = oK + CH * RSK;
-    static constexpr int oKt = oQ + (WITH_O ? CH * RSK : 0);
-    static constexpr int oA = oKt + (P::kBF16 ? DK * RST : 0);     // 10 lower tiles of -A
-    static constexpr int oT = oA + 10 * TILE;                       // 4 tiles T_bb - I
-    static constexpr int oPh = oT + 4 * TILE;                       // 10 lower tiles of P
-    static constexpr int oPl = oPh + (WITH_O ? 10 * TILE : 0);      // bf16 low parts
-    static constexpr int BUF = oPl + ((WITH_O && P::kBF16) ? 10 * TILE : 0);
-    static constexpr int oDiag = 2 * BUF;                           // 4 x 16x16 fp32
-    static constexpr int oMisc = oDiag + 4 * 256 * 4;
+    static constexpr int oQ = oK + CH * RBK;
+    static constexpr int oKt = oQ + (WITH_O ? CH * RBK : 0);
+    static constexpr int oA = oKt + (P::kBF16 ? DK * RBT : 0);  // -A
+    static constexpr int oT = oA + NTA * UNIT;                   // 4 tiles T_bb - I
+    static constexpr int oPh = oT + 4 * TILE;                    // P
+    static constexpr int oPl = oPh + (WITH_O ? NTA * UNIT : 0);  // bf16 low parts of P
+    static constexpr int BUF = oPl + ((WITH_O && P::kBF16) ? NTA * UNIT : 0);
+    static constexpr int DSTR = 260;                             // diagonal block stride (floats)
+    static constexpr int oDiag = 2 * BUF;
+    static constexpr int oMisc = oDiag + 4 * DSTR * 4;
     static constexpr int bytes = oMisc + 64;
 };
 
@@ -259,16 +270,17 @@ struct Lds {
 //     qk[i] = k_{16 tj + 4 (l/16) + i} . q_{16 ti + l%16},
 // i.e. entry (16 ti + l%16, 16 tj + 4 (l/16) + i) of K K^T and of Q K^T: four
 // consecutive columns of one row per lane, stored with one vector write.
-template <class P, int KBK, int RSK, bool WITH_O>
+template <class P, int KBK, int RBK, bool WITH_O>
 __device__ __forceinline__ void gram_t(const char *Ks, const char *Qs, int ti, int tj, int lane,
                                        f32x4 &kk, f32x4 &qk) {
     kk = f32x4{0.f, 0.f, 0.f, 0.f};
     qk = kk;
 #pragma unroll
     for (int kb = 0; kb < KBK; ++kb) {
-        const auto kj = frag_rm<RSK>(Ks, 16 * tj, kb, lane, typename P::E());
-        kk = mma(kk, kj, frag_rm<RSK>(Ks, 16 * ti, kb, lane, typename P::E()));
-        if constexpr (WITH_O) qk = mma(qk, kj, frag_rm<RSK>(Qs, 16 * ti, kb, lane, typename P::E()));
+        typedef typename P::Frag F;
+        const F kj = frag_sw<RBK, F>(Ks, 16 * tj, kb, lane);
+        kk = mma(kk, kj, frag_sw<RBK, F>(Ks, 16 * ti, kb, lane));
+        if constexpr (WITH_O) qk = mma(qk, kj, frag_sw<RBK, F>(Qs, 16 * ti, kb, lane));
     }
 }
 
@@ -285,7 +297,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
     constexpr int KBK = DK / P::KB;        // k-blocks over d_k
     constexpr int KBT = CH / P::KB;        // k-blocks over the chunk's tokens
     constexpr int NCB = DV / W;            // column blocks per head
-    constexpr int RBK = L::RBK, RSK = L::RSK, RST = L::RST;
+    constexpr int RBK = L::RBK;
     static_assert(L::bytes <= 160 * 1024, "LDS plan");
 
     __shared__ __attribute__((aligned(16))) char smem[L::bytes];
@@ -346,6 +358,12 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             gMisc[0] = row0;
             *pctr = 0;
             *pfail = 0;
+        }
+    }
+    if constexpr (P::kBF16) {   // the tile pairs' upper halves are zero and never written
+        for (int i = 16 * tid; i < L::BUF - L::oA; i += 16 * NTHR) {
+            *reinterpret_cast<u32x4 *>(smem + L::oA + i) = u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4 *>(smem + L::BUF + L::oA + i) = u32x4{0u, 0u, 0u, 0u};
         }
     }
     __syncthreads();
@@ -428,9 +446,9 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                 else sh = S[kb];
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
-                    X[tt] = mma(X[tt], frag_rm<RSK>(Ks, 16 * tt, kb, lane, E()), sh);
+                    X[tt] = mma(X[tt], frag_sw<RBK, Frag>(Ks, 16 * tt, kb, lane), sh);
                     if constexpr (WITH_O) {
-                        const Frag qf = frag_rm<RSK>(Qs, 16 * tt, kb, lane, E());
+                        const Frag qf = frag_sw<RBK, Frag>(Qs, 16 * tt, kb, lane);
                         OT[tt] = mma(OT[tt], sh, qf);
                         if constexpr (P::kBF16) OT[tt] = mma(OT[tt], sl, qf);
                     }
@@ -449,22 +467,18 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             // (I + A) U = Y by 16-row block forward substitution
             f32x4 U[4];
             if constexpr (P::kBF16) {
-                const uint16_t *At = reinterpret_cast<const uint16_t *>(buf + L::oA);
+                const char *Ad = buf + L::oA;
                 const uint16_t *Tt = reinterpret_cast<const uint16_t *>(buf + L::oT);
                 const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     f32x4 z = X[b];
                     if (b >= 1) {   // tiles (b, 0), (b, 1); U_1 is still zero when b = 1
-                        z = mma(z, frag_tiles(At, tri_index(b, 0), tri_index(b, 1), lane),
-                                bfrag_hi(U[0], b >= 2 ? U[1] : zero));
-                        if (b == 3)
-                            z = mma(z, frag_tiles(At, tri_index(3, 2), tri_index(3, 3), lane),
-                                    bfrag_hi(U[2], zero));
+                        z = mma(z, frag_dt(Ad, dt_index(b, 0), lane), bfrag_hi(U[0], b >= 2 ? U[1] : zero));
+                        if (b == 3) z = mma(z, frag_dt(Ad, dt_index(3, 1), lane), bfrag_hi(U[2], zero));
                     }
                     const bool odd = (b & 1) != 0;
-                    U[b] = mma(z, frag_tiles(Tt, odd ? -1 : b, odd ? b : -1, lane),
-                               odd ? bfrag_hi(zero, z) : bfrag_hi(z, zero));
+                    U[b] = mma(z, frag_half(Tt, b, odd, lane), odd ? bfrag_hi(zero, z) : bfrag_hi(z, zero));
                 }
             } else {
                 const float *At = reinterpret_cast<const float *>(buf + L::oA);
@@ -488,8 +502,8 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                     if constexpr (P::kBF16) bfrag_split(U[2 * kb], U[2 * kb + 1], uh[kb], ul[kb]);
                     else uh[kb] = U[kb];
                 }
-                const E *Ph = reinterpret_cast<const E *>(buf + L::oPh);
-                const E *Pl = reinterpret_cast<const E *>(buf + L::oPl);
+                const char *Ph = buf + L::oPh;
+                const char *Pl = buf + L::oPl;
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
                     OT[tt] *= gEs[16 * tt + lr];
@@ -497,14 +511,13 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                     for (int kb = 0; kb < KBT; ++kb) {
                         if (kb * P::KB < 16 * tt + 16) {
                             if constexpr (P::kBF16) {
-                                const int ta = tri_index(tt, 2 * kb);
-                                const int tb = (2 * kb + 1 <= tt) ? tri_index(tt, 2 * kb + 1) : -1;
-                                const Frag ph = frag_tiles(Ph, ta, tb, lane);
+                                const Frag ph = frag_dt(Ph, dt_index(tt, kb), lane);
                                 OT[tt] = mma(OT[tt], uh[kb], ph);
                                 OT[tt] = mma(OT[tt], ul[kb], ph);
-                                OT[tt] = mma(OT[tt], uh[kb], frag_tiles(Pl, ta, tb, lane));
+                                OT[tt] = mma(OT[tt], uh[kb], frag_dt(Pl, dt_index(tt, kb), lane));
                             } else {
-                                OT[tt] = mma(OT[tt], uh[kb], frag_tile(Ph, tri_index(tt, kb), lane));
+                                OT[tt] = mma(OT[tt], uh[kb],
+                                             frag_tile(reinterpret_cast<const float *>(Ph), tri_index(tt, kb), lane));
                             }
                         }
                     }
@@ -555,11 +568,11 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
 #pragma unroll
                     for (int kb = 0; kb < KBT; ++kb) {
                         if constexpr (P::kBF16) {
-                            const Frag kf = frag_rm<RST>(buf + L::oKt, 16 * rt, kb, lane, uint16_t());
+                            const Frag kf = frag_sw<L::RBT, Frag>(buf + L::oKt, 16 * rt, kb, lane);
                             s = mma(s, kf, dh[kb]);
                             s = mma(s, kf, dl[kb]);
                         } else {
-                            s = mma(s, frag_rm_cols<RSK>(Ks, 16 * rt, kb, lane), dh[kb]);
+                            s = mma(s, frag_cols_f32<RBK>(Ks, 16 * rt, kb, lane), dh[kb]);
                         }
                     }
                     S[rt] = s;
@@ -579,13 +592,17 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         // prep waves: chunk c + 1's operands while the state waves process chunk c
         const int pw = wave - NSW;                 // 0..NPW-1
         int target = 0;
-        constexpr int NCK = RBK / 16;              // 16-byte vectors per K (or Q) row
-        constexpr int RPJ = 64 * NPW / NCK;        // rows per load round
-        constexpr int NVT = CH / RPJ;              // load rounds per chunk
-        static_assert((64 * NPW) % NCK == 0 && CH % RPJ == 0, "vector map");
+        // K / Q staging: a thread moves "units" of a row; a bf16 unit is the two 16-byte
+        // vectors (columns 32b + 8q .. +7 and 32b + 16 + 8q .. +7) that make up logical
+        // chunks 4b + 2q and 4b + 2q + 1, an fp32 unit one vector (one chunk)
+        constexpr int VPU = P::kBF16 ? 2 : 1;                 // vectors per unit
+        constexpr int NPU = P::kBF16 ? DK / 16 : RBK / 16;    // units per row
+        constexpr int RPJ = 64 * NPW / NPU;                   // rows per round
+        constexpr int NR = CH / RPJ;                          // rounds per chunk
+        static_assert((64 * NPW) % NPU == 0 && CH % RPJ == 0 && RPJ % 16 == 0, "unit map");
         const uint32_t krow = (uint32_t)a.h_qk * (uint32_t)RBK;    // bytes per token
         const uint32_t grow = (uint32_t)a.h_v * 4u;
-        u32x4 kpf[NVT], qpf[NVT];
+        u32x4 kpf[NR * VPU], qpf[NR * VPU];
         uint32_t gpf = 0, bpf = 0;
         // the chunk starting at token cc of the window into registers (rows past the
         // window read as 0: g = b = 0 there)
@@ -598,13 +615,17 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             const int64_t koff = (t0 * a.h_qk + hk) * (int64_t)DK;
             const Rsrc rk = make_rsrc(kg + koff, ln * (int64_t)krow);
             const Rsrc rq = make_rsrc(qg + koff, ln * (int64_t)krow);
-            const uint32_t vo = (uint32_t)(pt / NCK) * krow + (uint32_t)(pt % NCK) * 16u;
+            const int pu = pt % NPU;
+            const uint32_t vo = (uint32_t)(pt / NPU) * krow +
+                                (uint32_t)(P::kBF16 ? 64 * (pu >> 1) + 16 * (pu & 1) : 16 * pu);
 #pragma unroll
-            for (int j = 0; j < NVT; ++j) {
-                kpf[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo + (uint32_t)(RPJ * j) * krow, 0, 0);
-                if (WITH_O)
-                    qpf[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, vo + (uint32_t)(RPJ * j) * krow, 0, 0);
-            }
+            for (int j = 0; j < NR; ++j)
+#pragma unroll
+                for (int v = 0; v < VPU; ++v) {
+                    const uint32_t o = vo + (uint32_t)(RPJ * j) * krow + 32u * v;
+                    kpf[VPU * j + v] = __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0);
+                    if (WITH_O) qpf[VPU * j + v] = __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0);
+                }
             if (pw == 0) {
                 const Rsrc rg = make_rsrc(a.g + t0 * a.h_v + h, ln * (int64_t)grow);
                 const Rsrc rb = make_rsrc(a.beta + t0 * a.h_v + h, ln * (int64_t)grow);
@@ -625,11 +646,27 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             float *gE = gH + CH, *gB = gE + CH, *gL = gB + CH, *gEs = gL + CH;
             int *gR = reinterpret_cast<int *>(gEs + CH);
             // ---- step 1: K, Q into LDS; gate scan; fetch the chunk after
+            {
+                const int pu = pt % NPU, row = pt / NPU;
 #pragma unroll
-            for (int j = 0; j < NVT; ++j) {
-                const int off = (pt / NCK + RPJ * j) * RSK + (pt % NCK) * 16;
-                *reinterpret_cast<u32x4 *>(Ks + off) = kpf[j];
-                if (WITH_O) *reinterpret_cast<u32x4 *>(Qs + off) = qpf[j];
+                for (int j = 0; j < NR; ++j) {
+                    if constexpr (P::kBF16) {
+                        const int c0 = 4 * (pu >> 1) + 2 * (pu & 1);
+                        const int o0 = chunk_at<RBK>(row + RPJ * j, c0), o1 = chunk_at<RBK>(row + RPJ * j, c0 + 1);
+                        const u32x4 a0 = kpf[2 * j], a1 = kpf[2 * j + 1];
+                        *reinterpret_cast<u32x4 *>(Ks + o0) = u32x4{a0.x, a0.y, a1.x, a1.y};
+                        *reinterpret_cast<u32x4 *>(Ks + o1) = u32x4{a0.z, a0.w, a1.z, a1.w};
+                        if (WITH_O) {
+                            const u32x4 b0 = qpf[2 * j], b1 = qpf[2 * j + 1];
+                            *reinterpret_cast<u32x4 *>(Qs + o0) = u32x4{b0.x, b0.y, b1.x, b1.y};
+                            *reinterpret_cast<u32x4 *>(Qs + o1) = u32x4{b0.z, b0.w, b1.z, b1.w};
+                        }
+                    } else {
+                        const int o = chunk_at<RBK>(row + RPJ * j, pu);
+                        *reinterpret_cast<u32x4 *>(Ks + o) = kpf[j];
+                        if (WITH_O) *reinterpret_cast<u32x4 *>(Qs + o) = qpf[j];
+                    }
+                }
             }
             if (pw == 0) {
                 const float gv = __uint_as_float(gpf), bv = __uint_as_float(bpf);
@@ -671,7 +708,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                     int ti, tj;
                     tri_tile(idx, ti, tj);
                     f32x4 kk, qk;
-                    gram_t<P, KBK, RSK, WITH_O>(Ks, Qs, ti, tj, lane, kk, qk);
+                    gram_t<P, KBK, RBK, WITH_O>(Ks, Qs, ti, tj, lane, kk, qk);
                     const int rr = 16 * ti + lr;              // row of this lane
                     const float hr = gH[rr], br = gB[rr];
                     const int rho = gR[rr];
@@ -684,19 +721,17 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                         av[e] = c < rr ? -br * gam * kk[e] : 0.f;
                         pv[e] = a.scale * gam * qk[e];
                     }
-                    const int eo = tri_index(ti, tj) * 256 + lr * 16 + 4 * lg;
-                    if (ti == tj) *reinterpret_cast<f32x4 *>(diag + ti * 256 + lr * 16 + 4 * lg) = av;
+                    if (ti == tj) *reinterpret_cast<f32x4 *>(diag + ti * L::DSTR + lr * 16 + 4 * lg) = av;
                     if constexpr (P::kBF16) {
-                        *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(buf + L::oA) + eo) =
-                            u32x2{pk_bf16(av[0], av[1]), pk_bf16(av[2], av[3])};
+                        const int eo = dt_index(ti, tj >> 1) * 1024 + dt_at(lr, lg) + 8 * (tj & 1);
+                        *reinterpret_cast<u32x2 *>(buf + L::oA + eo) = u32x2{pk_bf16(av[0], av[1]), pk_bf16(av[2], av[3])};
                         if constexpr (WITH_O) {
                             const u32x2 p01 = split2(pv[0], pv[1]), p23 = split2(pv[2], pv[3]);
-                            *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(buf + L::oPh) + eo) =
-                                u32x2{p01.x, p23.x};
-                            *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(buf + L::oPl) + eo) =
-                                u32x2{p01.y, p23.y};
+                            *reinterpret_cast<u32x2 *>(buf + L::oPh + eo) = u32x2{p01.x, p23.x};
+                            *reinterpret_cast<u32x2 *>(buf + L::oPl + eo) = u32x2{p01.y, p23.y};
                         }
                     } else {
+                        const int eo = tri_index(ti, tj) * 256 + lr * 16 + 4 * lg;
                         *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(buf + L::oA) + eo) = av;
                         if constexpr (WITH_O)
                             *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(buf + L::oPh) + eo) = pv;
@@ -704,24 +739,32 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                 }
             }
             if constexpr (P::kBF16) {
-                // K^T[dk][t] as packed token pairs, by the two waves with fewer Gram
-                // tiles: thread -> (token pair, 8-column block)
-                constexpr int NU = 32 * (DK / 8);
+                // K^T[dk][t] (same chunk layout, tokens permuted like the columns of K),
+                // by the two waves with fewer Gram tiles: thread -> (token pair, K chunk)
+                constexpr int NCK = RBK / 16;
+                constexpr int NU = 32 * NCK;
                 static_assert(NU % 128 == 0, "K^T map");
                 if (pw >= 2) {
 #pragma unroll
                     for (int j = 0; j < NU / 128; ++j) {
                         const int u = (pt - 128) + 128 * j;
-                        const int pr = u & 31, c8 = u >> 5;
-                        const u32x4 x0 = *reinterpret_cast<const u32x4 *>(Ks + (2 * pr) * RSK + 16 * c8);
-                        const u32x4 x1 = *reinterpret_cast<const u32x4 *>(Ks + (2 * pr + 1) * RSK + 16 * c8);
+                        const int pr = u & 31, ck = u >> 5;
+                        const u32x4 x0 = *reinterpret_cast<const u32x4 *>(Ks + chunk_at<RBK>(2 * pr, ck));
+                        const u32x4 x1 = *reinterpret_cast<const u32x4 *>(Ks + chunk_at<RBK>(2 * pr + 1, ck));
                         const uint32_t xs0[4] = {x0.x, x0.y, x0.z, x0.w}, xs1[4] = {x1.x, x1.y, x1.z, x1.w};
+                        // destination of the pair (2pr, 2pr + 1) inside a K^T row
+                        const int tq = (2 * pr) & 31;
+                        const int ct = 4 * (pr >> 4) + ((tq & 15) >> 2);
+                        const int pb = 2 * ((tq >= 16 ? 4 : 0) + (tq & 3));
+                        // element e of chunk ck is column (d_k) 32 (ck/4) + 4 (ck%4) + e (+12 for e >= 4)
+                        const int d0 = 32 * (ck >> 2) + 4 * (ck & 3);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const uint32_t lo = (xs0[e] & 0xffffu) | (xs1[e] << 16);
-                            const uint32_t hi = (xs0[e] >> 16) | (xs1[e] & 0xffff0000u);
-                            *reinterpret_cast<uint32_t *>(buf + L::oKt + (8 * c8 + 2 * e) * RST + 4 * pr) = lo;
-                            *reinterpret_cast<uint32_t *>(buf + L::oKt + (8 * c8 + 2 * e + 1) * RST + 4 * pr) = hi;
+                        for (int e = 0; e < 8; ++e) {
+                            const int d = d0 + (e < 4 ? e : 12 + e);
+                            const uint32_t w0 = xs0[e >> 1], w1 = xs1[e >> 1];
+                            const uint32_t val = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))
+                                                         : ((w0 & 0xffffu) | (w1 << 16));
+                            *reinterpret_cast<uint32_t *>(buf + L::oKt + chunk_at<L::RBT>(d, ct) + pb) = val;
                         }
                     }
                 }
@@ -732,7 +775,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             // lane = (block l/16, column l%16); stored as T_bb - I; four partial sums
             if (pw == 0) {
                 const int blk = lane >> 4, cidx = lane & 15;
-                const float *nb = diag + blk * 256;
+                const float *nb = diag + blk * L::DSTR;
                 float t[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
