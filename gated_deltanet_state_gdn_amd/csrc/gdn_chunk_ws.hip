@@ -240,7 +240,7 @@ __device__ __forceinline__ void prep_sync(int *ctr, int &target, int lane, int *
 
 // ---------------------------------------------------------------- LDS plan
 // Two chunk buffers (the state waves read one while the prep waves fill the other),
-// then the prep waves' fp32 diagonal blocks of -A, then a few words.
+// then a few words.
 template <int DK, class P, bool WITH_O>
 struct Lds {
     typedef typename P::E E;
@@ -258,9 +258,7 @@ struct Lds {
     static constexpr int oPh = oT + 4 * TILE;                    // P
     static constexpr int oPl = oPh + (WITH_O ? NTA * UNIT : 0);  // bf16 low parts of P
     static constexpr int BUF = oPl + ((WITH_O && P::kBF16) ? NTA * UNIT : 0);
-    static constexpr int DSTR = 260;                             // diagonal block stride (floats)
-    static constexpr int oDiag = 2 * BUF;
-    static constexpr int oMisc = oDiag + 4 * DSTR * 4;
+    static constexpr int oMisc = 2 * BUF;
     static constexpr int bytes = oMisc + 64;
 };
 
@@ -284,6 +282,139 @@ __device__ __forceinline__ void gram_t(const char *Ks, const char *Qs, int ti, i
     }
 }
 
+// ---------------------------------------------------------------- prep-wave pieces
+// Gates of one chunk, one token per lane: reset-aware inclusive scan of the log-gates
+// (H = sum of g since the last alpha = 0 token), e = exp(H) (0 once a reset occurred),
+// G_last = exp(H_63 - H) (0 before the chunk's last reset), rho = last reset position.
+struct Gates {
+    float h, e, b, l;
+    int rho;
+};
+__device__ __forceinline__ Gates gate_scan(float gv, float bv, int lane) {
+    const bool reset = gv == -__builtin_inff();
+    float hv = reset ? 0.f : gv;
+    int seg = reset ? 1 : 0;
+    int rho = reset ? lane : -1;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float ho = __shfl_up(hv, off);
+        const int so = __shfl_up(seg, off);
+        const int ro = __shfl_up(rho, off);
+        if (lane >= off) {
+            if (!seg) hv += ho;
+            seg |= so;
+            rho = ro > rho ? ro : rho;
+        }
+    }
+    const float hl = __shfl(hv, 63);
+    const int rl = __shfl(rho, 63);
+    Gates g;
+    g.h = hv;
+    g.e = rho < 0 ? __expf(hv) : 0.f;
+    g.b = bv;
+    g.l = rl <= lane ? __expf(hl - hv) : 0.f;
+    g.rho = rho;
+    return g;
+}
+
+// One Gram tile (ti, tj) of a chunk into -A and P = scale lower(Q K^T o G) (hi + lo for
+// bf16).  Lane l handles row 16 ti + l%16, columns 16 tj + 4 (l/16) + e; the -A values
+// are returned (for ti == tj: the diagonal block in the A-operand layout).
+template <int DK, class P, bool WITH_O, class L>
+__device__ __forceinline__ f32x4 gram_tile(char *buf, int ti, int tj, int lane, float scale) {
+    constexpr int KBK = DK / P::KB;
+    const int lr = lane & 15, lg = lane >> 4;
+    const float *gH = reinterpret_cast<const float *>(buf + L::oGate);
+    const float *gB = gH + 2 * CH;
+    const int *gR = reinterpret_cast<const int *>(gH + 5 * CH);
+    f32x4 kk, qk;
+    gram_t<P, KBK, L::RBK, WITH_O>(buf + L::oK, buf + L::oQ, ti, tj, lane, kk, qk);
+    const int rr = 16 * ti + lr;
+    const float hr = gH[rr], br = gB[rr];
+    const int rho = gR[rr];
+    const f32x4 hc = *reinterpret_cast<const f32x4 *>(gH + 16 * tj + 4 * lg);
+    f32x4 av, pv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int c = 16 * tj + 4 * lg + e;
+        // exp of every entry, then a select: no divergent branch (the unused ones may be inf)
+        const float ex = __expf(hr - hc[e]);
+        const float gam = (c <= rr && rho <= c) ? ex : 0.f;
+        av[e] = c < rr ? -br * gam * kk[e] : 0.f;
+        pv[e] = scale * gam * qk[e];
+    }
+    if constexpr (P::kBF16) {
+        const int eo = dt_index(ti, tj >> 1) * 1024 + dt_at(lr, lg) + 8 * (tj & 1);
+        *reinterpret_cast<u32x2 *>(buf + L::oA + eo) = u32x2{pk_bf16(av[0], av[1]), pk_bf16(av[2], av[3])};
+        if constexpr (WITH_O) {
+            const u32x2 p01 = split2(pv[0], pv[1]), p23 = split2(pv[2], pv[3]);
+            *reinterpret_cast<u32x2 *>(buf + L::oPh + eo) = u32x2{p01.x, p23.x};
+            *reinterpret_cast<u32x2 *>(buf + L::oPl + eo) = u32x2{p01.y, p23.y};
+        }
+    } else {
+        const int eo = tri_index(ti, tj) * 256 + lr * 16 + 4 * lg;
+        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(buf + L::oA) + eo) = av;
+        if constexpr (WITH_O) *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(buf + L::oPh) + eo) = pv;
+    }
+    return av;
+}
+
+// fp32 16x16x16 product on the matrix cores: D = C + X Y for X in the A-operand layout
+// (lane l: row l%16, columns 4 (l/16) + i) and Y in the accumulator layout (lane l:
+// rows 4 (l/16) + i, column l%16); D comes out in the accumulator layout.  Read the other
+// way round, mma(C, Y, X) gives C + X Y in the A-operand layout.
+__device__ __forceinline__ f32x4 mm16(f32x4 c, f32x4 x, f32x4 y) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(x[j], y[j], c, 0, 0, 0);
+    return c;
+}
+
+// T_bb - I for one 16x16 block from N = -A_bb (strictly lower, so N^16 = 0) in the
+// A-operand layout, as the product
+//     T = (I + A)^{-1} = (I - N)^{-1} = I + N + ... + N^15 = (I + N)(I + N^2)(I + N^4)(I + N^8),
+// every factor formed on the fp32 matrix cores in registers; stored in the A-operand
+// layout (lane l: row l%16, columns 4 (l/16) .. +3).
+template <class E>
+__device__ __forceinline__ void diag_inverse(f32x4 Nr, E *Tt, int lane) {
+    const int lr = lane & 15, lg = lane >> 4;
+    f32x4 I4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) I4[i] = (4 * lg + i == lr) ? 1.f : 0.f;   // I, either layout
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 Nc = mm16(zero, Nr, I4);          // N, accumulator layout
+    const f32x4 N2c = mm16(zero, Nr, Nc), N2r = mm16(zero, Nc, Nr);
+    const f32x4 N3r = mm16(zero, N2c, Nr);        // N N^2
+    const f32x4 N4c = mm16(zero, N2r, N2c), N4r = mm16(zero, N2c, N2r);
+    const f32x4 N8c = mm16(zero, N4r, N4c);
+    const f32x4 P1r = I4 + Nr + N2r + N3r;        // (I + N)(I + N^2)
+    const f32x4 P2r = mm16(P1r, N4c, P1r);        // P1 (I + N^4)
+    const f32x4 Tr = mm16(P2r, N8c, P2r);         // P2 (I + N^8)
+    const f32x4 Tm = Tr - I4;
+    E *row = Tt + lr * 16 + 4 * lg;
+    if constexpr (sizeof(E) == 2) {
+        *reinterpret_cast<u32x2 *>(row) = u32x2{pk_bf16(Tm[0], Tm[1]), pk_bf16(Tm[2], Tm[3])};
+    } else {
+        *reinterpret_cast<f32x4 *>(row) = Tm;
+    }
+}
+
+// The Gram tiles of prep wave PW, which owns diagonal block PW: its own block first
+// (then inverted in registers), the off-diagonal tiles after, in one basic block so the
+// inverse's dependent products overlap with the other tiles' work.
+//   wave 0: (0,0) (1,0) (3,0)   wave 1: (1,1) (2,0) (3,1)   wave 2: (2,2) (2,1)   wave 3: (3,3) (3,2)
+template <int PW, int DK, class P, bool WITH_O, class L>
+__device__ __forceinline__ void prep_tiles(char *buf, int lane, float scale) {
+    typedef typename P::E E;
+    const f32x4 Nr = gram_tile<DK, P, WITH_O, L>(buf, PW, PW, lane, scale);
+    constexpr int ti1 = PW == 0 ? 1 : PW == 1 ? 2 : PW == 2 ? 2 : 3;
+    constexpr int tj1 = PW == 0 ? 0 : PW == 1 ? 0 : PW == 2 ? 1 : 2;
+    gram_tile<DK, P, WITH_O, L>(buf, ti1, tj1, lane, scale);
+    if constexpr (PW < 2) gram_tile<DK, P, WITH_O, L>(buf, 3, PW, lane, scale);
+    __builtin_amdgcn_sched_barrier(0);
+    diag_inverse<E>(Nr, reinterpret_cast<E *>(buf + L::oT) + PW * 256, lane);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---------------------------------------------------------------- kernel
 template <int DK, int DV, int W, class P, bool WITH_O>
 __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(ChunkArgs a)
@@ -301,7 +432,6 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
     static_assert(L::bytes <= 160 * 1024, "LDS plan");
 
     __shared__ __attribute__((aligned(16))) char smem[L::bytes];
-    float *diag = reinterpret_cast<float *>(smem + L::oDiag);
     int64_t *gMisc = reinterpret_cast<int64_t *>(smem + L::oMisc);
     int *pctr = reinterpret_cast<int *>(smem + L::oMisc + 8);
     int *pfail = reinterpret_cast<int *>(smem + L::oMisc + 12);
@@ -604,14 +734,22 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         const uint32_t grow = (uint32_t)a.h_v * 4u;
         u32x4 kpf[NR * VPU], qpf[NR * VPU];
         uint32_t gpf = 0, bpf = 0;
+        Gates gt = {0.f, 0.f, 0.f, 0.f, -1};
+        constexpr int GW = NPW - 1;                // the wave that owns the gates
         // the chunk starting at token cc of the window into registers (rows past the
-        // window read as 0: g = b = 0 there)
+        // window read as 0: g = b = 0 there; a chunk past the window reads nothing)
         auto fetch = [&](int64_t cc) {
             int lane = lane0;
             asm volatile("" : "+v"(lane));
             const int pt = 64 * pw + lane;
             const int64_t ln = (rn - cc) < CH ? (rn - cc) : CH;
             const int64_t t0 = wbeg + cc;
+            if (pw == GW) {   // first, so that waiting for them waits for nothing else
+                const Rsrc rg = make_rsrc(a.g + t0 * a.h_v + h, ln * (int64_t)grow);
+                const Rsrc rb = make_rsrc(a.beta + t0 * a.h_v + h, ln * (int64_t)grow);
+                gpf = __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)lane * grow, 0, 0);
+                bpf = __builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)lane * grow, 0, 0);
+            }
             const int64_t koff = (t0 * a.h_qk + hk) * (int64_t)DK;
             const Rsrc rk = make_rsrc(kg + koff, ln * (int64_t)krow);
             const Rsrc rq = make_rsrc(qg + koff, ln * (int64_t)krow);
@@ -626,26 +764,20 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                     kpf[VPU * j + v] = __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0);
                     if (WITH_O) qpf[VPU * j + v] = __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0);
                 }
-            if (pw == 0) {
-                const Rsrc rg = make_rsrc(a.g + t0 * a.h_v + h, ln * (int64_t)grow);
-                const Rsrc rb = make_rsrc(a.beta + t0 * a.h_v + h, ln * (int64_t)grow);
-                gpf = __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)lane * grow, 0, 0);
-                bpf = __builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)lane * grow, 0, 0);
-            }
         };
 
+        // prepare chunk cc into buffer cc & 1:
+        //   step 1: K, Q (fetched one chunk earlier) and the gates (scanned one chunk
+        //           earlier) into LDS; fetch chunk cc + 1
+        //   step 2: after the prep waves' barrier, each wave's Gram tiles and diagonal
+        //           inverse; K^T (waves 2, 3); the gate scan of chunk cc + 1 (wave GW)
         auto prep = [&](int64_t cc) {
             int lane = lane0;
             asm volatile("" : "+v"(lane));
-            const int lr = lane & 15, lg = lane >> 4;
             const int pt = 64 * pw + lane;
             char *buf = smem + (cc & 1) * L::BUF;
             char *Ks = buf + L::oK;
             char *Qs = buf + L::oQ;
-            float *gH = reinterpret_cast<float *>(buf + L::oGate);
-            float *gE = gH + CH, *gB = gE + CH, *gL = gB + CH, *gEs = gL + CH;
-            int *gR = reinterpret_cast<int *>(gEs + CH);
-            // ---- step 1: K, Q into LDS; gate scan; fetch the chunk after
             {
                 const int pu = pt % NPU, row = pt / NPU;
 #pragma unroll
@@ -668,75 +800,23 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                     }
                 }
             }
-            if (pw == 0) {
-                const float gv = __uint_as_float(gpf), bv = __uint_as_float(bpf);
-                // reset-aware inclusive scan: H = sum of g since the last alpha = 0 token
-                const bool reset = gv == -__builtin_inff();
-                float hv = reset ? 0.f : gv;
-                int seg = reset ? 1 : 0;
-                int rho = reset ? lane : -1;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float ho = __shfl_up(hv, off);
-                    const int so = __shfl_up(seg, off);
-                    const int ro = __shfl_up(rho, off);
-                    if (lane >= off) {
-                        if (!seg) hv += ho;
-                        seg |= so;
-                        rho = ro > rho ? ro : rho;
-                    }
-                }
-                const float hl = __shfl(hv, 63);
-                const int rl = __shfl(rho, 63);
-                const float ev = rho < 0 ? __expf(hv) : 0.f;
-                gH[lane] = hv;
-                gE[lane] = ev;
-                gEs[lane] = a.scale * ev;
-                gB[lane] = bv;
-                gR[lane] = rho;
-                gL[lane] = rl <= lane ? __expf(hl - hv) : 0.f;
+            if (pw == GW) {
+                float *gH = reinterpret_cast<float *>(buf + L::oGate);
+                gH[lane] = gt.h;
+                gH[CH + lane] = gt.e;
+                gH[2 * CH + lane] = gt.b;
+                gH[3 * CH + lane] = gt.l;
+                gH[4 * CH + lane] = a.scale * gt.e;
+                reinterpret_cast<int *>(gH + 5 * CH)[lane] = gt.rho;
             }
-            fetch((cc + 1) * CH);   // past the window: an empty buffer, no access
+            fetch((cc + 1) * CH);
             prep_sync(pctr, target, lane, pfail);
 
-            // ---- step 2: Gram tiles -> -A (tiles, and fp32 diagonal blocks for the
-            // inverses) and P = scale lower(Q K^T o G) (hi + lo); K^T
-            // (tile indices are compile-time: every LDS address folds into an offset)
-#pragma unroll
-            for (int idx = 0; idx < 10; ++idx) {
-                if (idx % NPW == pw) {
-                    int ti, tj;
-                    tri_tile(idx, ti, tj);
-                    f32x4 kk, qk;
-                    gram_t<P, KBK, RBK, WITH_O>(Ks, Qs, ti, tj, lane, kk, qk);
-                    const int rr = 16 * ti + lr;              // row of this lane
-                    const float hr = gH[rr], br = gB[rr];
-                    const int rho = gR[rr];
-                    const f32x4 hc = *reinterpret_cast<const f32x4 *>(gH + 16 * tj + 4 * lg);
-                    f32x4 av, pv;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int c = 16 * tj + 4 * lg + e;
-                        const float gam = (c <= rr && rho <= c) ? __expf(hr - hc[e]) : 0.f;
-                        av[e] = c < rr ? -br * gam * kk[e] : 0.f;
-                        pv[e] = a.scale * gam * qk[e];
-                    }
-                    if (ti == tj) *reinterpret_cast<f32x4 *>(diag + ti * L::DSTR + lr * 16 + 4 * lg) = av;
-                    if constexpr (P::kBF16) {
-                        const int eo = dt_index(ti, tj >> 1) * 1024 + dt_at(lr, lg) + 8 * (tj & 1);
-                        *reinterpret_cast<u32x2 *>(buf + L::oA + eo) = u32x2{pk_bf16(av[0], av[1]), pk_bf16(av[2], av[3])};
-                        if constexpr (WITH_O) {
-                            const u32x2 p01 = split2(pv[0], pv[1]), p23 = split2(pv[2], pv[3]);
-                            *reinterpret_cast<u32x2 *>(buf + L::oPh + eo) = u32x2{p01.x, p23.x};
-                            *reinterpret_cast<u32x2 *>(buf + L::oPl + eo) = u32x2{p01.y, p23.y};
-                        }
-                    } else {
-                        const int eo = tri_index(ti, tj) * 256 + lr * 16 + 4 * lg;
-                        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(buf + L::oA) + eo) = av;
-                        if constexpr (WITH_O)
-                            *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(buf + L::oPh) + eo) = pv;
-                    }
-                }
+            switch (pw) {
+            case 0: prep_tiles<0, DK, P, WITH_O, L>(buf, lane, a.scale); break;
+            case 1: prep_tiles<1, DK, P, WITH_O, L>(buf, lane, a.scale); break;
+            case 2: prep_tiles<2, DK, P, WITH_O, L>(buf, lane, a.scale); break;
+            default: prep_tiles<3, DK, P, WITH_O, L>(buf, lane, a.scale); break;
             }
             if constexpr (P::kBF16) {
                 // K^T[dk][t] (same chunk layout, tokens permuted like the columns of K),
@@ -769,36 +849,12 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                     }
                 }
             }
-            prep_sync(pctr, target, lane, pfail);
-
-            // ---- step 3: T_bb = (I + A_bb)^{-1} by forward substitution, one wave:
-            // lane = (block l/16, column l%16); stored as T_bb - I; four partial sums
-            if (pw == 0) {
-                const int blk = lane >> 4, cidx = lane & 15;
-                const float *nb = diag + blk * L::DSTR;
-                float t[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-                    for (int j4 = 0; j4 < (i + 3) / 4; ++j4) {
-                        const f32x4 av = *reinterpret_cast<const f32x4 *>(nb + i * 16 + 4 * j4);
-                        if (4 * j4 + 0 < i) s0 += av[0] * t[4 * j4 + 0];
-                        if (4 * j4 + 1 < i) s1 += av[1] * t[4 * j4 + 1];
-                        if (4 * j4 + 2 < i) s2 += av[2] * t[4 * j4 + 2];
-                        if (4 * j4 + 3 < i) s3 += av[3] * t[4 * j4 + 3];
-                    }
-                    t[i] = i < cidx ? 0.f : (i == cidx ? 1.f : (s0 + s1) + (s2 + s3));
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                E *Tt = reinterpret_cast<E *>(buf + L::oT) + blk * 256 + cidx;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) st_e(Tt + i * 16, i == cidx ? 0.f : t[i]);
-            }
+            if (pw == GW) gt = gate_scan(__uint_as_float(gpf), __uint_as_float(bpf), lane);
         };
 
         if (nch > 0) {
             fetch(0);
+            if (pw == GW) gt = gate_scan(__uint_as_float(gpf), __uint_as_float(bpf), lane);
             prep(0);
         }
         sync_lds();                                  // chunk 0 prepared
