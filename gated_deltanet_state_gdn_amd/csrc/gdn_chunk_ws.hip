@@ -262,26 +262,6 @@ struct Lds {
     static constexpr int bytes = oMisc + 64;
 };
 
-// Gram tile (ti, tj) of one chunk, computed as (K_tj K_ti^T) and (K_tj Q_ti^T) so that
-// element i of lane l is
-//     kk[i] = k_{16 tj + 4 (l/16) + i} . k_{16 ti + l%16},
-//     qk[i] = k_{16 tj + 4 (l/16) + i} . q_{16 ti + l%16},
-// i.e. entry (16 ti + l%16, 16 tj + 4 (l/16) + i) of K K^T and of Q K^T: four
-// consecutive columns of one row per lane, stored with one vector write.
-template <class P, int KBK, int RBK, bool WITH_O>
-__device__ __forceinline__ void gram_t(const char *Ks, const char *Qs, int ti, int tj, int lane,
-                                       f32x4 &kk, f32x4 &qk) {
-    kk = f32x4{0.f, 0.f, 0.f, 0.f};
-    qk = kk;
-#pragma unroll
-    for (int kb = 0; kb < KBK; ++kb) {
-        typedef typename P::Frag F;
-        const F kj = frag_sw<RBK, F>(Ks, 16 * tj, kb, lane);
-        kk = mma(kk, kj, frag_sw<RBK, F>(Ks, 16 * ti, kb, lane));
-        if constexpr (WITH_O) qk = mma(qk, kj, frag_sw<RBK, F>(Qs, 16 * ti, kb, lane));
-    }
-}
-
 // ---------------------------------------------------------------- prep-wave pieces
 // Gates of one chunk, one token per lane: reset-aware inclusive scan of the log-gates
 // (H = sum of g since the last alpha = 0 token), e = exp(H) (0 once a reset occurred),
@@ -317,22 +297,56 @@ __device__ __forceinline__ Gates gate_scan(float gv, float bv, int lane) {
     return g;
 }
 
-// One Gram tile (ti, tj) of a chunk into -A and P = scale lower(Q K^T o G) (hi + lo for
-// bf16).  Lane l handles row 16 ti + l%16, columns 16 tj + 4 (l/16) + e; the -A values
-// are returned (for ti == tj: the diagonal block in the A-operand layout).
+// One Gram tile (ti, tj) of a chunk, in three stages so that a wave can overlap the
+// LDS latency of one tile with the work of the previous one:
+//   tile_load  every fragment and gate value the tile needs, issued together;
+//   tile_mma   K_tj K_ti^T and K_tj Q_ti^T on the matrix cores;
+//   tile_store -A and P = scale lower(Q K^T o G) (hi + lo for bf16) into LDS.
+// The products are formed as K_tj K_ti^T and K_tj Q_ti^T, so that element e of lane l is
+//     kk[e] = k_{16 tj + 4 (l/16) + e} . k_{16 ti + l%16},
+//     qk[e] = k_{16 tj + 4 (l/16) + e} . q_{16 ti + l%16},
+// entry (16 ti + l%16, 16 tj + 4 (l/16) + e) of K K^T and of Q K^T: four consecutive
+// columns of one row per lane, stored with one vector write.  The -A values are
+// returned (for ti == tj: the diagonal block in the A-operand layout).
+template <class P, int KBK>
+struct TileIn {
+    typename P::Frag kj[KBK], ki[KBK], qi[KBK];
+    f32x4 hc;
+    float hr, br;
+    int rho;
+};
 template <int DK, class P, bool WITH_O, class L>
-__device__ __forceinline__ f32x4 gram_tile(char *buf, int ti, int tj, int lane, float scale) {
+__device__ __forceinline__ void tile_load(TileIn<P, DK / P::KB> &t, const char *buf, int ti, int tj, int lane) {
     constexpr int KBK = DK / P::KB;
-    const int lr = lane & 15, lg = lane >> 4;
+    typedef typename P::Frag F;
     const float *gH = reinterpret_cast<const float *>(buf + L::oGate);
-    const float *gB = gH + 2 * CH;
-    const int *gR = reinterpret_cast<const int *>(gH + 5 * CH);
-    f32x4 kk, qk;
-    gram_t<P, KBK, L::RBK, WITH_O>(buf + L::oK, buf + L::oQ, ti, tj, lane, kk, qk);
+#pragma unroll
+    for (int kb = 0; kb < KBK; ++kb) {
+        t.kj[kb] = frag_sw<L::RBK, F>(buf + L::oK, 16 * tj, kb, lane);
+        t.ki[kb] = frag_sw<L::RBK, F>(buf + L::oK, 16 * ti, kb, lane);
+        if constexpr (WITH_O) t.qi[kb] = frag_sw<L::RBK, F>(buf + L::oQ, 16 * ti, kb, lane);
+    }
+    const int rr = 16 * ti + (lane & 15);
+    t.hr = gH[rr];
+    t.br = gH[2 * CH + rr];
+    t.rho = reinterpret_cast<const int *>(gH + 5 * CH)[rr];
+    t.hc = *reinterpret_cast<const f32x4 *>(gH + 16 * tj + 4 * (lane >> 4));
+}
+template <int DK, class P, bool WITH_O>
+__device__ __forceinline__ void tile_mma(const TileIn<P, DK / P::KB> &t, f32x4 &kk, f32x4 &qk) {
+    kk = f32x4{0.f, 0.f, 0.f, 0.f};
+    qk = kk;
+#pragma unroll
+    for (int kb = 0; kb < DK / P::KB; ++kb) {
+        kk = mma(kk, t.kj[kb], t.ki[kb]);
+        if constexpr (WITH_O) qk = mma(qk, t.kj[kb], t.qi[kb]);
+    }
+}
+template <int DK, class P, bool WITH_O, class L>
+__device__ __forceinline__ f32x4 tile_store(char *buf, float hr, float br, int rho, f32x4 hc, f32x4 kk,
+                                            f32x4 qk, int ti, int tj, int lane, float scale) {
+    const int lr = lane & 15, lg = lane >> 4;
     const int rr = 16 * ti + lr;
-    const float hr = gH[rr], br = gB[rr];
-    const int rho = gR[rr];
-    const f32x4 hc = *reinterpret_cast<const f32x4 *>(gH + 16 * tj + 4 * lg);
     f32x4 av, pv;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -359,36 +373,49 @@ __device__ __forceinline__ f32x4 gram_tile(char *buf, int ti, int tj, int lane, 
     return av;
 }
 
-// fp32 16x16x16 product on the matrix cores: D = C + X Y for X in the A-operand layout
-// (lane l: row l%16, columns 4 (l/16) + i) and Y in the accumulator layout (lane l:
-// rows 4 (l/16) + i, column l%16); D comes out in the accumulator layout.  Read the other
-// way round, mma(C, Y, X) gives C + X Y in the A-operand layout.
+// 16x16x16 product on the matrix cores with bf16 (fp32 for fp32 inputs) operands and
+// fp32 accumulation:
+// D = C + X Y for X in the A-operand layout (lane l: row l%16, columns 4 (l/16) + i) and
+// Y in the accumulator layout (lane l: rows 4 (l/16) + i, column l%16); D comes out in the
+// accumulator layout.  Read the other way round, mm16(C, Y, X) gives C + X Y in the
+// A-operand layout.
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+__device__ __forceinline__ i16x4 pk4(f32x4 x) {
+    return __builtin_bit_cast(i16x4, u32x2{pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3])});
+}
+template <bool BF16>
 __device__ __forceinline__ f32x4 mm16(f32x4 c, f32x4 x, f32x4 y) {
+    if constexpr (BF16) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pk4(x), pk4(y), c, 0, 0, 0);
+    } else {   // fp32 operands for fp32 inputs (four 16x16x4 steps)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(x[j], y[j], c, 0, 0, 0);
-    return c;
+        for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(x[j], y[j], c, 0, 0, 0);
+        return c;
+    }
 }
 
 // T_bb - I for one 16x16 block from N = -A_bb (strictly lower, so N^16 = 0) in the
 // A-operand layout, as the product
 //     T = (I + A)^{-1} = (I - N)^{-1} = I + N + ... + N^15 = (I + N)(I + N^2)(I + N^4)(I + N^8),
-// every factor formed on the fp32 matrix cores in registers; stored in the A-operand
-// layout (lane l: row l%16, columns 4 (l/16) .. +3).
+// every factor formed in registers on the matrix cores (bf16 operands for bf16 inputs:
+// T - I is stored in bf16 for the solve anyway); stored in the A-operand layout (lane l:
+// row l%16, columns 4 (l/16) .. +3).
 template <class E>
 __device__ __forceinline__ void diag_inverse(f32x4 Nr, E *Tt, int lane) {
+    constexpr bool BF = sizeof(E) == 2;
     const int lr = lane & 15, lg = lane >> 4;
     f32x4 I4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) I4[i] = (4 * lg + i == lr) ? 1.f : 0.f;   // I, either layout
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    const f32x4 Nc = mm16(zero, Nr, I4);          // N, accumulator layout
-    const f32x4 N2c = mm16(zero, Nr, Nc), N2r = mm16(zero, Nc, Nr);
-    const f32x4 N3r = mm16(zero, N2c, Nr);        // N N^2
-    const f32x4 N4c = mm16(zero, N2r, N2c), N4r = mm16(zero, N2c, N2r);
-    const f32x4 N8c = mm16(zero, N4r, N4c);
-    const f32x4 P1r = I4 + Nr + N2r + N3r;        // (I + N)(I + N^2)
-    const f32x4 P2r = mm16(P1r, N4c, P1r);        // P1 (I + N^4)
-    const f32x4 Tr = mm16(P2r, N8c, P2r);         // P2 (I + N^8)
+    const f32x4 Nc = mm16<BF>(zero, Nr, I4);          // N, accumulator layout
+    const f32x4 N2c = mm16<BF>(zero, Nr, Nc), N2r = mm16<BF>(zero, Nc, Nr);
+    const f32x4 N3r = mm16<BF>(zero, N2c, Nr);        // N N^2
+    const f32x4 N4c = mm16<BF>(zero, N2r, N2c), N4r = mm16<BF>(zero, N2c, N2r);
+    const f32x4 N8c = mm16<BF>(zero, N4r, N4c);
+    const f32x4 P1r = I4 + Nr + N2r + N3r;            // (I + N)(I + N^2)
+    const f32x4 P2r = mm16<BF>(P1r, N4c, P1r);        // P1 (I + N^4)
+    const f32x4 Tr = mm16<BF>(P2r, N8c, P2r);         // P2 (I + N^8)
     const f32x4 Tm = Tr - I4;
     E *row = Tt + lr * 16 + 4 * lg;
     if constexpr (sizeof(E) == 2) {
@@ -398,18 +425,35 @@ __device__ __forceinline__ void diag_inverse(f32x4 Nr, E *Tt, int lane) {
     }
 }
 
-// The Gram tiles of prep wave PW, which owns diagonal block PW: its own block first
-// (then inverted in registers), the off-diagonal tiles after, in one basic block so the
-// inverse's dependent products overlap with the other tiles' work.
+// The Gram tiles of prep wave PW, which owns diagonal block PW (its own block first, then
+// inverted in registers), software-pipelined: the next tile's fragments are in flight
+// while the current one is finished.  The stages are kept in order with scheduling
+// barriers; the inverse's fp32 products are also kept apart from the bf16 Gram products
+// (interleaving the two in one schedule gave wrong results).
 //   wave 0: (0,0) (1,0) (3,0)   wave 1: (1,1) (2,0) (3,1)   wave 2: (2,2) (2,1)   wave 3: (3,3) (3,2)
 template <int PW, int DK, class P, bool WITH_O, class L>
 __device__ __forceinline__ void prep_tiles(char *buf, int lane, float scale) {
     typedef typename P::E E;
-    const f32x4 Nr = gram_tile<DK, P, WITH_O, L>(buf, PW, PW, lane, scale);
-    constexpr int ti1 = PW == 0 ? 1 : PW == 1 ? 2 : PW == 2 ? 2 : 3;
-    constexpr int tj1 = PW == 0 ? 0 : PW == 1 ? 0 : PW == 2 ? 1 : 2;
-    gram_tile<DK, P, WITH_O, L>(buf, ti1, tj1, lane, scale);
-    if constexpr (PW < 2) gram_tile<DK, P, WITH_O, L>(buf, 3, PW, lane, scale);
+    constexpr int KBK = DK / P::KB;
+    constexpr int NT = PW < 2 ? 3 : 2;
+    constexpr int TI[3] = {PW, PW == 0 ? 1 : PW == 1 ? 2 : PW == 2 ? 2 : 3, 3};
+    constexpr int TJ[3] = {PW, PW == 0 ? 0 : PW == 1 ? 0 : PW == 2 ? 1 : 2, PW};
+    TileIn<P, KBK> in;
+    f32x4 kk, qk, Nr;
+    tile_load<DK, P, WITH_O, L>(in, buf, TI[0], TJ[0], lane);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        __builtin_amdgcn_sched_barrier(0);
+        tile_mma<DK, P, WITH_O>(in, kk, qk);
+        const float hr = in.hr, br = in.br;
+        const int rho = in.rho;
+        const f32x4 hc = in.hc;
+        __builtin_amdgcn_sched_barrier(0);
+        if (n + 1 < NT) tile_load<DK, P, WITH_O, L>(in, buf, TI[n + 1], TJ[n + 1], lane);
+        __builtin_amdgcn_sched_barrier(0);
+        const f32x4 av = tile_store<DK, P, WITH_O, L>(buf, hr, br, rho, hc, kk, qk, TI[n], TJ[n], lane, scale);
+        if (n == 0) Nr = av;
+    }
     __builtin_amdgcn_sched_barrier(0);
     diag_inverse<E>(Nr, reinterpret_cast<E *>(buf + L::oT) + PW * 256, lane);
     __builtin_amdgcn_sched_barrier(0);
