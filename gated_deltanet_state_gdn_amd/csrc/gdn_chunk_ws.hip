@@ -23,7 +23,7 @@
 //     The outputs are formed transposed (O^T = S^T Q^T + U^T P^T), which puts four
 //     consecutive d_v entries of one token in a lane: one vector store per 16 tokens.
 //   * four prep waves: everything that does not depend on S, one chunk ahead -- the
-//     chunk's K, Q (and K^T) in LDS, the gate scan, the Gram products forming -A and
+//     chunk's K and Q in LDS, the gate scan, the Gram products forming -A and
 //     P, and the diagonal-block inverses.
 // One workgroup barrier per chunk hands a prepared buffer to the state waves; the
 // prep waves order their own steps with a counter in LDS.
@@ -129,15 +129,20 @@ __device__ __forceinline__ float v_at(typename Raw<P>::T v) {
 }
 
 // ---------------------------------------------------------------- LDS layouts
-// Operand matrices (K, Q, K^T) are row-major with RB-byte rows of 16-byte chunks and no
-// padding: logical chunk c of row r sits at chunk c ^ swz(r), which spreads the 16 rows
-// that one fragment read touches over all banks (16-byte reads run at full rate).
-// bf16 columns are permuted inside every 32-column block so that one chunk holds a whole
-// fragment: logical chunk 4 kb + g carries columns 32 kb + {4g..4g+3, 16+4g..16+4g+3},
-// the contraction indices that pair with accumulator rows 4g + i of two 16-row tiles.
-// fp32 keeps the natural order (logical chunk 4 kb + g = columns 16 kb + 4g .. 4g+3).
+// Operand matrices (K, Q) are row-major with RB-byte rows of 16-byte chunks and no
+// padding: logical chunk c of row r sits at chunk c ^ swz(r).  bf16 columns are permuted
+// inside every 32-column block so that one chunk holds a whole fragment: logical chunk
+// 4 kb + g carries columns 32 kb + {4g..4g+3, 16+4g..16+4g+3}, the contraction indices
+// that pair with accumulator rows 4g + i of two 16-row tiles; an aligned group of four
+// columns is always 8 contiguous bytes.  fp32 keeps the natural order (logical chunk
+// 4 kb + g = columns 16 kb + 4g .. 4g+3).
+// The swizzle (swap of the two 2-bit halves of the row index for 256-byte rows) keeps
+// both access patterns free of bank conflicts: 16-byte row fragments (16 rows, one
+// logical chunk) and the 8-byte transposing reads of K^T fragments (4 rows x 4 chunks).
 template <int RB>
-__device__ __forceinline__ int swz(int r) { return RB == 256 ? (r & 15) : ((r >> 1) & 7); }
+__device__ __forceinline__ int swz(int r) {
+    return RB == 256 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
 template <int RB>
 __device__ __forceinline__ int chunk_at(int r, int c) { return r * RB + 16 * (c ^ swz<RB>(r)); }
 
@@ -147,6 +152,24 @@ template <int RB, class F>
 __device__ __forceinline__ F frag_sw(const char *M, int r0, int kb, int lane) {
     return __builtin_bit_cast(
         F, *reinterpret_cast<const u32x4 *>(M + chunk_at<RB>(r0 + (lane & 15), 4 * kb + (lane >> 4))));
+}
+// bf16 fragment of K^T for one 16x16x32 product, read transposed from the row-major K:
+// lane l gets K[32 kb + {4 (l/16) + i, 16 + 4 (l/16) + i}][16 rt + l%16], i = 0..3.  The
+// transposing read hands lane n of every 16-lane group column n%4 of rows
+// {n/4, n/4 + 4, n/4 + 8, n/4 + 12} of the 16 x 4 block whose row m is the 8 bytes lane m
+// points at; lane m = 4 y + x of group g points at token 32 kb + 4 g + y (+16 for the
+// second half), columns 16 rt + 4 x .. +3.
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+template <int RB>
+__device__ __forceinline__ bf16x8 frag_kt(const char *K, int rt, int kb, int lane) {
+    const int m = lane & 15;
+    const int row = 32 * kb + 4 * (lane >> 4) + (m >> 2);
+    const char *p = K + chunk_at<RB>(row, 4 * (rt >> 1) + (m & 3)) + 8 * (rt & 1);
+    typedef __attribute__((address_space(3))) i16x4 *lds_i16x4;
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)p);
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(p + 16 * RB));
+    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+    return __builtin_bit_cast(bf16x8, u32x4{ua.x, ua.y, ub.x, ub.y});
 }
 // fp32 fragment of M^T (the rows of M are the contraction index): lane l gives column
 // c0 + l%16 and rows 16 kb + 4 (l/16) + i.
@@ -245,15 +268,13 @@ template <int DK, class P, bool WITH_O>
 struct Lds {
     typedef typename P::E E;
     static constexpr int RBK = DK * (int)sizeof(E);          // K / Q row bytes
-    static constexpr int RBT = CH * 2;                         // K^T row bytes (bf16)
     static constexpr int TILE = 256 * (int)sizeof(E);          // one 16x16 tile
     static constexpr int NTA = P::kBF16 ? 6 : 10;              // tile pairs (bf16) / tiles (fp32)
     static constexpr int UNIT = P::kBF16 ? 1024 : TILE;
     static constexpr int oGate = 0;                            // H, e, b, G_last, scale e, rho
     static constexpr int oK = 6 * CH * 4;
     static constexpr int oQ = oK + CH * RBK;
-    static constexpr int oKt = oQ + (WITH_O ? CH * RBK : 0);
-    static constexpr int oA = oKt + (P::kBF16 ? DK * RBT : 0);  // -A
+    static constexpr int oA = oQ + (WITH_O ? CH * RBK : 0);     // -A
     static constexpr int oT = oA + NTA * UNIT;                   // 4 tiles T_bb - I
     static constexpr int oPh = oT + 4 * TILE;                    // P
     static constexpr int oPl = oPh + (WITH_O ? NTA * UNIT : 0);  // bf16 low parts of P
@@ -379,7 +400,6 @@ __device__ __forceinline__ f32x4 tile_store(char *buf, float hr, float br, int r
 // Y in the accumulator layout (lane l: rows 4 (l/16) + i, column l%16); D comes out in the
 // accumulator layout.  Read the other way round, mm16(C, Y, X) gives C + X Y in the
 // A-operand layout.
-typedef __attribute__((ext_vector_type(4))) short i16x4;
 __device__ __forceinline__ i16x4 pk4(f32x4 x) {
     return __builtin_bit_cast(i16x4, u32x2{pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3])});
 }
@@ -742,7 +762,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
 #pragma unroll
                     for (int kb = 0; kb < KBT; ++kb) {
                         if constexpr (P::kBF16) {
-                            const Frag kf = frag_sw<L::RBT, Frag>(buf + L::oKt, 16 * rt, kb, lane);
+                            const Frag kf = frag_kt<RBK>(Ks, rt, kb, lane);
                             s = mma(s, kf, dh[kb]);
                             s = mma(s, kf, dl[kb]);
                         } else {
@@ -814,7 +834,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         //   step 1: K, Q (fetched one chunk earlier) and the gates (scanned one chunk
         //           earlier) into LDS; fetch chunk cc + 1
         //   step 2: after the prep waves' barrier, each wave's Gram tiles and diagonal
-        //           inverse; K^T (waves 2, 3); the gate scan of chunk cc + 1 (wave GW)
+        //           inverse; the gate scan of chunk cc + 1 (wave GW)
         auto prep = [&](int64_t cc) {
             int lane = lane0;
             asm volatile("" : "+v"(lane));
@@ -861,37 +881,6 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             case 1: prep_tiles<1, DK, P, WITH_O, L>(buf, lane, a.scale); break;
             case 2: prep_tiles<2, DK, P, WITH_O, L>(buf, lane, a.scale); break;
             default: prep_tiles<3, DK, P, WITH_O, L>(buf, lane, a.scale); break;
-            }
-            if constexpr (P::kBF16) {
-                // K^T[dk][t] (same chunk layout, tokens permuted like the columns of K),
-                // by the two waves with fewer Gram tiles: thread -> (token pair, K chunk)
-                constexpr int NCK = RBK / 16;
-                constexpr int NU = 32 * NCK;
-                static_assert(NU % 128 == 0, "K^T map");
-                if (pw >= 2) {
-#pragma unroll
-                    for (int j = 0; j < NU / 128; ++j) {
-                        const int u = (pt - 128) + 128 * j;
-                        const int pr = u & 31, ck = u >> 5;
-                        const u32x4 x0 = *reinterpret_cast<const u32x4 *>(Ks + chunk_at<RBK>(2 * pr, ck));
-                        const u32x4 x1 = *reinterpret_cast<const u32x4 *>(Ks + chunk_at<RBK>(2 * pr + 1, ck));
-                        const uint32_t xs0[4] = {x0.x, x0.y, x0.z, x0.w}, xs1[4] = {x1.x, x1.y, x1.z, x1.w};
-                        // destination of the pair (2pr, 2pr + 1) inside a K^T row
-                        const int tq = (2 * pr) & 31;
-                        const int ct = 4 * (pr >> 4) + ((tq & 15) >> 2);
-                        const int pb = 2 * ((tq >= 16 ? 4 : 0) + (tq & 3));
-                        // element e of chunk ck is column (d_k) 32 (ck/4) + 4 (ck%4) + e (+12 for e >= 4)
-                        const int d0 = 32 * (ck >> 2) + 4 * (ck & 3);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int d = d0 + (e < 4 ? e : 12 + e);
-                            const uint32_t w0 = xs0[e >> 1], w1 = xs1[e >> 1];
-                            const uint32_t val = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))
-                                                         : ((w0 & 0xffffu) | (w1 << 16));
-                            *reinterpret_cast<uint32_t *>(buf + L::oKt + chunk_at<L::RBT>(d, ct) + pb) = val;
-                        }
-                    }
-                }
             }
             if (pw == GW) gt = gate_scan(__uint_as_float(gpf), __uint_as_float(bpf), lane);
         };
