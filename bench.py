@@ -220,8 +220,8 @@ def traffic_from_profile(kernel_ms):
     """HBM bytes per launch from the committed counter summary, if it was taken on the
     kernel source as it is now (else None)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "gdn_chunk_traffic.json")
-    src = os.path.join(ROOT, "gated_deltanet_state_gdn_amd", "csrc", "gdn_chunk.hip")
+    path = os.path.join(ROOT, "profiles", "gdn_chunk_ws_traffic.json")
+    src = os.path.join(ROOT, "gated_deltanet_state_gdn_amd", "csrc", "gdn_chunk_ws.hip")
     try:
         rec = json.load(open(path))
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()

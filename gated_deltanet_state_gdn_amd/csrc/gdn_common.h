@@ -25,12 +25,9 @@ struct ChunkArgs {
     float scale;
 };
 
-// Launch the chunk kernel for the given dtype / head dims.  Returns hipSuccess or
-// the launch error; hipErrorNotSupported for an unsupported combination.
-hipError_t launch_chunk(const ChunkArgs &a, int bf16, int d_k, int d_v, bool with_o,
-                        hipStream_t stream);
-
-// Warp-specialised variant: state waves and prep waves on double-buffered LDS.
+// Launch the chunk kernel (state waves and prep waves on double-buffered LDS) for the
+// given dtype / head dims.  Returns hipSuccess or the launch error;
+// hipErrorNotSupported for an unsupported combination.
 hipError_t launch_chunk_ws(const ChunkArgs &a, int bf16, int d_k, int d_v, bool with_o,
                            hipStream_t stream);
 
