@@ -61,7 +61,7 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 
 constexpr int CH = 64;       // chunk length (tokens)
-constexpr int NPW = 4;       // prep waves per workgroup
+constexpr int NPW = 8;       // prep waves per workgroup
 
 __device__ __forceinline__ uint16_t f2bf(float f) {
     __bf16 h = (__bf16)f;                  // round to nearest even (v_cvt_pk_bf16_f32)
@@ -445,38 +445,43 @@ __device__ __forceinline__ void diag_inverse(f32x4 Nr, E *Tt, int lane) {
     }
 }
 
-// The Gram tiles of prep wave PW, which owns diagonal block PW (its own block first, then
-// inverted in registers), software-pipelined: the next tile's fragments are in flight
-// while the current one is finished.  The stages are kept in order with scheduling
-// barriers; the inverse's fp32 products are also kept apart from the bf16 Gram products
-// (interleaving the two in one schedule gave wrong results).
-//   wave 0: (0,0) (1,0) (3,0)   wave 1: (1,1) (2,0) (3,1)   wave 2: (2,2) (2,1)   wave 3: (3,3) (3,2)
+// The Gram tiles of prep wave PW: waves 0..3 own diagonal block PW (formed, then inverted
+// in registers); waves 4..6 two off-diagonal tiles each; wave 7 none (it owns the gates).
+//   wave 4: (1,0) (2,0)   wave 5: (2,1) (3,0)   wave 6: (3,1) (3,2)
+// Software-pipelined: the next tile's fragments are in flight while the current one is
+// finished.  The stages are kept in order with scheduling barriers; the inverse's
+// products are also kept apart from the Gram products (interleaving the two in one
+// schedule gave wrong results).
 template <int PW, int DK, class P, bool WITH_O, class L>
 __device__ __forceinline__ void prep_tiles(char *buf, int lane, float scale) {
     typedef typename P::E E;
     constexpr int KBK = DK / P::KB;
-    constexpr int NT = PW < 2 ? 3 : 2;
-    constexpr int TI[3] = {PW, PW == 0 ? 1 : PW == 1 ? 2 : PW == 2 ? 2 : 3, 3};
-    constexpr int TJ[3] = {PW, PW == 0 ? 0 : PW == 1 ? 0 : PW == 2 ? 1 : 2, PW};
-    TileIn<P, KBK> in;
-    f32x4 kk, qk, Nr;
-    tile_load<DK, P, WITH_O, L>(in, buf, TI[0], TJ[0], lane);
+    constexpr int NT = PW < 4 ? 1 : PW < 7 ? 2 : 0;
+    constexpr int TI[2] = {PW < 4 ? PW : PW == 4 ? 1 : PW == 5 ? 2 : 3, PW == 4 ? 2 : 3};
+    constexpr int TJ[2] = {PW < 4 ? PW : PW == 4 ? 0 : PW == 5 ? 1 : 1, PW == 4 ? 0 : PW == 5 ? 0 : 2};
+    if constexpr (NT > 0) {
+        TileIn<P, KBK> in;
+        f32x4 kk, qk, Nr;
+        tile_load<DK, P, WITH_O, L>(in, buf, TI[0], TJ[0], lane);
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-        __builtin_amdgcn_sched_barrier(0);
-        tile_mma<DK, P, WITH_O>(in, kk, qk);
-        const float hr = in.hr, br = in.br;
-        const int rho = in.rho;
-        const f32x4 hc = in.hc;
-        __builtin_amdgcn_sched_barrier(0);
-        if (n + 1 < NT) tile_load<DK, P, WITH_O, L>(in, buf, TI[n + 1], TJ[n + 1], lane);
-        __builtin_amdgcn_sched_barrier(0);
-        const f32x4 av = tile_store<DK, P, WITH_O, L>(buf, hr, br, rho, hc, kk, qk, TI[n], TJ[n], lane, scale);
-        if (n == 0) Nr = av;
+        for (int n = 0; n < NT; ++n) {
+            __builtin_amdgcn_sched_barrier(0);
+            tile_mma<DK, P, WITH_O>(in, kk, qk);
+            const float hr = in.hr, br = in.br;
+            const int rho = in.rho;
+            const f32x4 hc = in.hc;
+            __builtin_amdgcn_sched_barrier(0);
+            if (n + 1 < NT) tile_load<DK, P, WITH_O, L>(in, buf, TI[n + 1], TJ[n + 1], lane);
+            __builtin_amdgcn_sched_barrier(0);
+            const f32x4 av = tile_store<DK, P, WITH_O, L>(buf, hr, br, rho, hc, kk, qk, TI[n], TJ[n], lane, scale);
+            if (n == 0) Nr = av;
+        }
+        if constexpr (PW < 4) {
+            __builtin_amdgcn_sched_barrier(0);
+            diag_inverse<E>(Nr, reinterpret_cast<E *>(buf + L::oT) + PW * 256, lane);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    diag_inverse<E>(Nr, reinterpret_cast<E *>(buf + L::oT) + PW * 256, lane);
-    __builtin_amdgcn_sched_barrier(0);
 }
 
 // ---------------------------------------------------------------- kernel
@@ -791,9 +796,11 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         // chunks 4b + 2q and 4b + 2q + 1, an fp32 unit one vector (one chunk)
         constexpr int VPU = P::kBF16 ? 2 : 1;                 // vectors per unit
         constexpr int NPU = P::kBF16 ? DK / 16 : RBK / 16;    // units per row
-        constexpr int RPJ = 64 * NPW / NPU;                   // rows per round
-        constexpr int NR = CH / RPJ;                          // rounds per chunk
-        static_assert((64 * NPW) % NPU == 0 && CH % RPJ == 0 && RPJ % 16 == 0, "unit map");
+        constexpr int UT = CH * NPU;                          // units per matrix
+        constexpr int TH = 64 * NPW;                          // prep threads
+        constexpr int RPJ = TH / NPU;                         // rows per round
+        constexpr int NR = (UT + TH - 1) / TH;                // rounds per chunk
+        static_assert(TH % NPU == 0 && (UT <= TH || UT % TH == 0), "unit map");
         const uint32_t krow = (uint32_t)a.h_qk * (uint32_t)RBK;    // bytes per token
         const uint32_t grow = (uint32_t)a.h_v * 4u;
         u32x4 kpf[NR * VPU], qpf[NR * VPU];
@@ -820,14 +827,16 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             const int pu = pt % NPU;
             const uint32_t vo = (uint32_t)(pt / NPU) * krow +
                                 (uint32_t)(P::kBF16 ? 64 * (pu >> 1) + 16 * (pu & 1) : 16 * pu);
+            if (UT >= TH || pt < UT) {   // with fewer units than threads, the last waves idle
 #pragma unroll
-            for (int j = 0; j < NR; ++j)
+                for (int j = 0; j < NR; ++j)
 #pragma unroll
-                for (int v = 0; v < VPU; ++v) {
-                    const uint32_t o = vo + (uint32_t)(RPJ * j) * krow + 32u * v;
-                    kpf[VPU * j + v] = __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0);
-                    if (WITH_O) qpf[VPU * j + v] = __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0);
-                }
+                    for (int v = 0; v < VPU; ++v) {
+                        const uint32_t o = vo + (uint32_t)(RPJ * j) * krow + 32u * v;
+                        kpf[VPU * j + v] = __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0);
+                        if (WITH_O) qpf[VPU * j + v] = __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0);
+                    }
+            }
         };
 
         // prepare chunk cc into buffer cc & 1:
@@ -842,7 +851,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             char *buf = smem + (cc & 1) * L::BUF;
             char *Ks = buf + L::oK;
             char *Qs = buf + L::oQ;
-            {
+            if (UT >= TH || pt < UT) {
                 const int pu = pt % NPU, row = pt / NPU;
 #pragma unroll
                 for (int j = 0; j < NR; ++j) {
@@ -880,7 +889,11 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             case 0: prep_tiles<0, DK, P, WITH_O, L>(buf, lane, a.scale); break;
             case 1: prep_tiles<1, DK, P, WITH_O, L>(buf, lane, a.scale); break;
             case 2: prep_tiles<2, DK, P, WITH_O, L>(buf, lane, a.scale); break;
-            default: prep_tiles<3, DK, P, WITH_O, L>(buf, lane, a.scale); break;
+            case 3: prep_tiles<3, DK, P, WITH_O, L>(buf, lane, a.scale); break;
+            case 4: prep_tiles<4, DK, P, WITH_O, L>(buf, lane, a.scale); break;
+            case 5: prep_tiles<5, DK, P, WITH_O, L>(buf, lane, a.scale); break;
+            case 6: prep_tiles<6, DK, P, WITH_O, L>(buf, lane, a.scale); break;
+            default: break;
             }
             if (pw == GW) gt = gate_scan(__uint_as_float(gpf), __uint_as_float(bpf), lane);
         };
