@@ -194,12 +194,145 @@ def main():
         torch.cuda.synchronize()
         out["relerr_replay_vs_full"] = {"max": float(rel.max()), "median": float(rel.median()),
                                         "nonfinite": int(nf.sum())}
-        del op, Sp
+        del op
+        if len(set(w.lengths)) == 1:
+            out["suffix_prefill"] = suffix_leg(w, inp, gdn, stream, ws, pms / layers, n_seqs)
+        out["adaptive_replay_len"] = adaptive_leg(w, inp, gdn, stream, ws, Sp, layers, with_o)
+        out["transfer_overlap"] = overlap_leg(step, stream, kern_ms)
+        del Sp
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, with_o, args.cpu_seconds)
 
     print(json.dumps(out), flush=True)
+
+
+def _time(fn, stream, reps):
+    import torch
+    fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def suffix_leg(w, inp, gdn, stream, ws, full_prefill_ms_per_layer, n_seqs, suffix=1024):
+    """Replay over a matched prefix of L - suffix tokens (10 % budget, state only) plus a
+    prefill of the suffix from the rebuilt state, against the full prefill of all L
+    tokens: the linear-attention part of time-to-first-token after a cache hit."""
+    import numpy as np
+    import torch
+    import workloads as W
+    L = int(w.lengths[0])
+    Lp = L - suffix
+    rp = W.replay_len(Lp, 0.10)
+    dev = inp["q"].device
+    # sequence n's matched prefix ends `suffix` tokens before its end; the prefix of
+    # sequence n > 0 starts with the previous layer's suffix, which a replay of rp <= Lp
+    # tokens never reads
+    cu_p = torch.tensor([0] + [n * L + Lp for n in range(n_seqs)], dtype=torch.int32, device=dev)
+    r_p = torch.full((n_seqs,), rp, dtype=torch.int32, device=dev)
+    idx = torch.cat([torch.arange(n * L + Lp, (n + 1) * L, device=dev) for n in range(n_seqs)])
+    suf = {k: inp[k].index_select(0, idx).contiguous() for k in ("q", "k", "v", "g", "beta")}
+    cu_s = torch.arange(0, (n_seqs + 1) * suffix, suffix, dtype=torch.int32, device=dev)
+    S_r = torch.empty((n_seqs, w.h_v, w.d_k, w.d_v), dtype=torch.float32, device=dev)
+    S_f = torch.empty_like(S_r)
+    o_f = torch.empty((n_seqs * suffix, w.h_v, w.d_v), dtype=inp["q"].dtype, device=dev)
+    q, k, v, g, beta = (inp[x] for x in ("q", "k", "v", "g", "beta"))
+
+    def rebuild():
+        gdn.gdn_replay(q, k, v, g, beta, cu_p, r_p, total_out_tokens=n_seqs * rp, S_out=S_r,
+                       o_out=None, ws=ws, scale=w.scale, stream=stream)
+
+    def rest():
+        gdn.gdn_prefill(suf["q"], suf["k"], suf["v"], suf["g"], suf["beta"], cu_s, S0=S_r,
+                        S_out=S_f, o_out=o_f, ws=ws, scale=w.scale, stream=stream)
+
+    def both():
+        rebuild()
+        rest()
+
+    reps = 5
+    t_rep = _time(rebuild, stream, reps) / n_seqs
+    t_suf = _time(rest, stream, reps) / n_seqs
+    t_both = _time(both, stream, reps) / n_seqs
+    return {"matched_prefix": Lp, "replay_tokens": rp, "suffix_tokens": suffix,
+            "replay_state_only_us_per_layer": t_rep * 1e3,
+            "suffix_prefill_us_per_layer": t_suf * 1e3,
+            "replay_plus_suffix_us_per_layer": t_both * 1e3,
+            "full_prefill_us_per_layer": full_prefill_ms_per_layer * 1e3,
+            "speedup_vs_full_prefill": full_prefill_ms_per_layer / t_both}
+
+
+def adaptive_leg(w, inp, gdn, stream, ws, S_full, layers, with_o, eps=1e-3):
+    """Replay length chosen per sequence from the gates (prod alpha <= eps in every
+    v-head), then the replay with that length, and its error against full prefill."""
+    import torch
+    g, cu = inp["g"], inp["cu_seqlens"]
+    n = int(cu.shape[0]) - 1
+    r = torch.empty(n, dtype=torch.int32, device=g.device)
+    sel = lambda: gdn.gdn_adaptive_replay_len(g, cu, eps=eps, r_out=r, ws=ws, stream=stream)
+    t_sel = _time(sel, stream, 5)
+    rh = r.cpu().numpy()
+    tot = int(rh.sum())
+    S = torch.empty_like(S_full)
+    o = torch.empty((tot, w.h_v, w.d_v), dtype=inp["q"].dtype, device=g.device) if with_o else None
+    rep = lambda: gdn.gdn_replay(inp["q"], inp["k"], inp["v"], g, inp["beta"], cu, r,
+                                 total_out_tokens=tot, S_out=S, o_out=o, ws=ws, scale=w.scale,
+                                 stream=stream)
+    t_rep = _time(rep, stream, 5)
+    rel, nf = gdn.gdn_state_relerr(S, S_full, stream=stream)
+    torch.cuda.synchronize()
+    return {"eps": eps, "r_mean": float(rh.mean()), "r_min": int(rh.min()), "r_max": int(rh.max()),
+            "select_us_per_layer": t_sel * 1e3 / layers,
+            "replay_us_per_layer": t_rep * 1e3 / layers,
+            "relerr_vs_full": {"max": float(rel.max()), "median": float(rel.median()),
+                               "nonfinite": int(nf.sum())}}
+
+
+def overlap_leg(step, stream, replay_ms, fa_layers=12, kv_heads=2, head_dim=256, tokens=32768):
+    """A second stream copies a pinned host buffer the size of a hybrid stack's
+    full-attention KV cache (fa_layers x K and V x kv_heads x head_dim, bf16, for the
+    matched prefix) to the device while the replay runs on its own stream."""
+    import torch
+    nbytes = fa_layers * 2 * kv_heads * head_dim * 2 * tokens
+    host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    host.fill_(7)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()              # default priority
+    copy = lambda: dst.copy_(host, non_blocking=True)
+
+    def run(overlap):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        if overlap:
+            side.wait_event(e0)
+            with torch.cuda.stream(side):
+                copy()
+            step()
+            done = torch.cuda.Event()
+            done.record(side)
+            stream.wait_event(done)
+        else:
+            with torch.cuda.stream(stream):
+                copy()
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    run(False); run(True)
+    ser = min(run(False) for _ in range(3))
+    ovl = min(run(True) for _ in range(3))
+    with torch.cuda.stream(stream):
+        t_copy = _time(copy, stream, 3)
+    del host, dst
+    return {"fa_kv_bytes": nbytes, "copy_ms": t_copy, "replay_ms": replay_ms,
+            "serialized_ms": ser, "overlapped_ms": ovl, "saved_frac": 1.0 - ovl / ser}
 
 
 def copy_calibration(mib: int, reps: int):

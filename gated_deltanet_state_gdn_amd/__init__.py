@@ -20,6 +20,7 @@ from ._lib import (GDN_BF16, GDN_F32, GdnDesc, GdnError, GDN_ERR_DEVICE_INPUT, G
                    LIB_PATH, load)
 
 __all__ = ["gdn_replay", "gdn_prefill", "gdn_state_relerr", "gdn_device_status",
+           "gdn_adaptive_replay_len",
            "gdn_workspace_bytes", "gdn_replay_len", "gdn_status_str", "gdn_abi_version",
            "GdnError", "make_desc", "workspace", "LIB_PATH", "load"]
 
@@ -146,3 +147,24 @@ def gdn_device_status(ws, stream=None) -> int:
     code = load().gdn_device_status(_ptr(ws), _stream(stream), ctypes.byref(out))
     _check(code, "gdn_device_status")
     return int(out.value)
+
+
+def gdn_adaptive_replay_len(g, cu_seqlens, *, eps: float, r_min: int = 0, r_max: int = 2**31 - 1,
+                            r_out=None, ws=None, stream=None):
+    """Per-sequence replay length from the gates (see include/gdn.h). ``g``: [T, h_v] fp32.
+
+    Returns r_out (int32 [n_seqs], on the device), usable as gdn_replay's ``r``.
+    """
+    lib = load()
+    n = int(cu_seqlens.shape[0]) - 1
+    d = GdnDesc()
+    d.n_seqs, d.h_v, d.total_tokens = n, int(g.shape[1]), int(g.shape[0])
+    if r_out is None:
+        r_out = torch.empty(max(n, 0), dtype=torch.int32, device=g.device)
+    if ws is None:
+        ws = workspace(d, g.device)
+    code = lib.gdn_adaptive_replay_len(ctypes.byref(d), _ptr(g), _ptr(cu_seqlens), float(eps),
+                                       int(r_min), int(r_max), _ptr(r_out), _ptr(ws), ws.numel(),
+                                       _stream(stream))
+    _check(code, "gdn_adaptive_replay_len")
+    return r_out

@@ -14,7 +14,8 @@ ABI_VERSION = 1
 
 # every symbol include/gdn.h declares
 EXPORTS = ("gdn_abi_version", "gdn_status_str", "gdn_replay_len", "gdn_workspace_bytes",
-           "gdn_replay", "gdn_prefill", "gdn_state_relerr", "gdn_device_status")
+           "gdn_replay", "gdn_prefill", "gdn_state_relerr", "gdn_device_status",
+           "gdn_adaptive_replay_len")
 
 
 class GdnDesc(ctypes.Structure):
@@ -61,6 +62,8 @@ def load() -> ctypes.CDLL:
     lib.gdn_state_relerr.restype = i32
     lib.gdn_device_status.argtypes = [vp, vp, ctypes.POINTER(i32)]
     lib.gdn_device_status.restype = i32
+    lib.gdn_adaptive_replay_len.argtypes = [dptr, vp, vp, ctypes.c_double, i32, i32, vp, vp, sz, vp]
+    lib.gdn_adaptive_replay_len.restype = i32
     if lib.gdn_abi_version() != ABI_VERSION:
         raise ImportError("libgdn.so ABI version mismatch")
     _lib = lib

@@ -105,6 +105,14 @@ int32_t run(const gdn_desc *d, const void *q, const void *k, const void *v, cons
     return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
+// per-(sequence, v-head) lengths of gdn_adaptive_replay_len, after the status word
+size_t adaptive_scratch_bytes(const gdn_desc *d)
+{
+    if (!d || d->n_seqs <= 0 || d->h_v <= 0) return 0;
+    const size_t b = (size_t)d->n_seqs * (size_t)d->h_v * sizeof(int32_t);
+    return (b + 255) & ~(size_t)255;
+}
+
 }  // namespace
 
 extern "C" {
@@ -140,8 +148,7 @@ int32_t gdn_replay_len(int32_t L, double rho)
 
 size_t gdn_workspace_bytes(const gdn_desc *desc)
 {
-    (void)desc;
-    return kWorkspaceBytes;
+    return kWorkspaceBytes + adaptive_scratch_bytes(desc);
 }
 
 int32_t gdn_replay(const gdn_desc *d, const void *q, const void *k, const void *v, const float *g,
@@ -173,6 +180,32 @@ int32_t gdn_state_relerr(const float *S_a, const float *S_ref, int64_t n_states,
         return GDN_ERR_ALIGN;
     const hipError_t e = gdn::launch_relerr(S_a, S_ref, n_states, d_k * d_v, relerr_out,
                                             nonfinite_out, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+int32_t gdn_adaptive_replay_len(const gdn_desc *d, const float *g, const int32_t *cu_seqlens,
+                                double eps, int32_t r_min, int32_t r_max, int32_t *r_out,
+                                void *ws, size_t ws_bytes, void *stream)
+{
+    if (!d) return GDN_ERR_NULL;
+    if (d->n_seqs < 0 || d->h_v <= 0 || d->total_tokens < 0 || d->total_tokens > 0x7fffffffLL ||
+        r_min < 0 || r_max < r_min || !(eps > 0.0)) {
+        debug("adaptive replay length: bad sizes, clamp range or eps");
+        return GDN_ERR_SHAPE;
+    }
+    if (!cu_seqlens || !r_out || !ws || (d->total_tokens > 0 && !g)) return GDN_ERR_NULL;
+    if (!aligned16(g) || !aligned16(ws) || ((uintptr_t)cu_seqlens & 3u) || ((uintptr_t)r_out & 3u))
+        return GDN_ERR_ALIGN;
+    if (ws_bytes < kWorkspaceBytes + adaptive_scratch_bytes(d)) return GDN_ERR_WORKSPACE;
+    if (d->n_seqs == 0) return GDN_OK;
+    // threshold on the window's summed log-gates, in units of 2^-32 nats
+    int64_t thr = 0;
+    if (eps < 1.0) thr = (int64_t)floor(log(eps) * 4294967296.0);   // >= -745 * 2^32
+    int32_t *scratch = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(ws) + kWorkspaceBytes);
+    const hipError_t e = gdn::launch_adaptive(g, cu_seqlens, d->n_seqs, d->h_v, d->total_tokens,
+                                              thr, r_min, r_max, scratch, r_out,
+                                              reinterpret_cast<int32_t *>(ws),
+                                              reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 

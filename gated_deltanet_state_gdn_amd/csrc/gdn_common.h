@@ -34,6 +34,12 @@ hipError_t launch_chunk_ws(const ChunkArgs &a, int bf16, int d_k, int d_v, bool 
 hipError_t launch_relerr(const float *A, const float *B, int64_t n_states, int32_t elems,
                          float *relerr, int32_t *nonfinite, hipStream_t stream);
 
+// Adaptive replay length: r_head [n_seqs * h_v] is scratch (per-head lengths), r_out
+// [n_seqs] the clamped per-sequence maximum; thr = floor(ln(eps) * 2^32).
+hipError_t launch_adaptive(const float *g, const int32_t *cu, int32_t n_seqs, int32_t h_v,
+                           int64_t total_tokens, int64_t thr, int32_t r_min, int32_t r_max,
+                           int32_t *r_head, int32_t *r_out, int32_t *status, hipStream_t stream);
+
 constexpr int32_t kStatusOk = 0;
 constexpr int32_t kStatusBadInput = 8;   // == GDN_ERR_DEVICE_INPUT
 

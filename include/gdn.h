@@ -90,7 +90,8 @@ const char *gdn_status_str(int32_t status);
  * prefix (Tail-Replay abstract; technical summary, "Resultados"). */
 int32_t gdn_replay_len(int32_t L, double rho);
 
-/* (host) Workspace bytes a call with this descriptor needs (>= 256, a status word). */
+/* (host) Workspace bytes a call with this descriptor needs: 256 (a status word), plus
+ * n_seqs * h_v * 4 rounded up to 256 for gdn_adaptive_replay_len. */
 size_t gdn_workspace_bytes(const gdn_desc *desc);
 
 /* Tail replay: for every sequence n and v-head h, run the recurrence from S = 0 over
@@ -118,6 +119,31 @@ int32_t gdn_prefill(const gdn_desc *desc, const void *q, const void *k, const vo
  * non-finite entries of S_a[s].  States are d_k x d_v fp32 blocks. */
 int32_t gdn_state_relerr(const float *S_a, const float *S_ref, int64_t n_states, int32_t d_k,
                          int32_t d_v, float *relerr_out, int32_t *nonfinite_out, void *stream);
+
+/* Adaptive replay length.  The replayed state differs from the full-prefill state by
+ * the older state carried through the window's per-token maps alpha_t (I - beta_t k_t
+ * k_t^T), whose product has norm at most prod alpha_t for unit keys and beta in
+ * [0, 1]; the gated updates attenuate distant tokens (Tail-Replay, arXiv 2608.30310,
+ * abstract; technical summary, "Mecanismos Principais"), while the pages fix r as a
+ * 5-10 % budget ("Resultados").  This picks r per sequence from the gates instead:
+ *
+ *     r_h[n] = the smallest r in [0, min(L_n, r_max)] with sum over the last r tokens
+ *              of g[t, h] <= ln(eps)   (i.e. prod alpha <= eps), or min(L_n, r_max);
+ *     r_out[n] = clamp(max_h r_h[n], min(r_min, L_n), min(r_max, L_n)),
+ *
+ * so ||S_full - S_replay||_F <= eps ||S_before||_F in every head whenever r_out[n] is
+ * below the cap.  The comparison is exact: each g is rounded to a multiple of 2^-32
+ * nats (g >= 0 or NaN counts as 0; g <= -2^20, including -inf, as -2^20) and summed in
+ * integers against floor(ln(eps) * 2^32); eps >= 1 gives r_h = 0.
+ * desc: n_seqs, h_v and total_tokens are read (the other fields are ignored).
+ * g [T, h_v] fp32 and cu_seqlens [n_seqs+1] are device arrays; r_out [n_seqs] (device,
+ * int32) can be passed straight to gdn_replay.  The workspace must hold
+ * gdn_workspace_bytes(desc) bytes; its status word reports GDN_ERR_DEVICE_INPUT for a
+ * bad cu_seqlens (those sequences get r_out = 0).  Host errors: eps <= 0 or NaN,
+ * r_min < 0 or r_max < r_min -> GDN_ERR_SHAPE. */
+int32_t gdn_adaptive_replay_len(const gdn_desc *desc, const float *g, const int32_t *cu_seqlens,
+                                double eps, int32_t r_min, int32_t r_max, int32_t *r_out,
+                                void *workspace, size_t workspace_bytes, void *stream);
 
 /* (host, synchronising) Wait for `stream` and read the status word the last compute
  * call that launched work wrote into `workspace`: GDN_OK or GDN_ERR_DEVICE_INPUT.

@@ -7,6 +7,10 @@ it; the product path must never reach it.
 The arithmetic lives in ``gdn_oracle.c`` (plain C, double precision, token by
 token).  This wrapper only widens inputs exactly to float64 and passes pointers.
 
+``adaptive_replay_len`` is plain Python on exact integers (the definition written out:
+walk back from the last token, sum the rounded log-gates, stop at the first window
+whose sum is at or below the threshold).
+
 Pins (see ``tests/test_oracle_pins.py``): explicit-matrix brute force, exact
 rational arithmetic, closed forms (alpha=1/beta=0, single token, orthonormal keys
 with beta=1, repeated key overwrite), and invariants (alpha=0 makes replay equal
@@ -16,6 +20,7 @@ duplicated heads, packing order).  No function here is "parity unpinned".
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 import threading
@@ -160,3 +165,55 @@ def chain_inputs(inp: dict, seq: int, head: int, window: str = "replay"):
     return (widen(inp["q"][sl, hk:hk + 1]), widen(inp["k"][sl, hk:hk + 1]),
             widen(inp["v"][sl, head:head + 1]), widen(inp["g"][sl, head:head + 1]),
             widen(inp["beta"][sl, head:head + 1]))
+
+
+GATE_UNIT = 2 ** 32          # log-gates are counted in units of 2^-32 nats
+GATE_FLOOR = -(2 ** 52)      # a gate at or below -2^20 nats (alpha ~ 0) counts as -2^20
+
+
+def quantized_log_gates(g) -> list:
+    """Each g (fp32) rounded once, half to even, to an integer number of 2^-32 nats.
+
+    g >= 0 or NaN counts as 0 (no attenuation); g <= -2^20 nats, -inf included, as
+    -2^20 nats.  Returns nested Python lists of exact integers, shape of ``g``.
+    """
+    x = widen(g)
+    out = np.where(~(x < 0.0), 0.0, np.where(x <= -2.0 ** 20, float(GATE_FLOOR), np.rint(x * GATE_UNIT)))
+    return out.astype(np.int64).tolist()
+
+
+def adaptive_replay_len(g, cu_seqlens, eps, r_min=0, r_max=2 ** 31 - 1):
+    """Per-sequence replay length chosen from the gates.
+
+    The replayed state misses the older state carried through the window, whose
+    propagation has norm at most prod alpha_t over the window for unit keys and beta in
+    [0, 1] (Tail-Replay, abstract: gated updates attenuate distant tokens).  For every
+    sequence n and v-head h, r_h is the smallest r in [0, min(L_n, r_max)] whose last-r
+    log-gate sum (in 2^-32 nat units, ``quantized_log_gates``) is at most
+    floor(ln(eps) * 2^32), else min(L_n, r_max); the result is max_h r_h clamped to
+    [min(r_min, L_n), min(r_max, L_n)].  eps >= 1 makes the empty window qualify.
+    """
+    if not (eps > 0.0):
+        raise ValueError("eps must be positive")
+    thr = math.floor(math.log(eps) * GATE_UNIT) if eps < 1.0 else 0
+    qg = quantized_log_gates(g)
+    cu = [int(c) for c in cu_seqlens]
+    H = len(qg[0]) if qg else 0
+    out = []
+    for n in range(len(cu) - 1):
+        b, e = cu[n], cu[n + 1]
+        L = e - b
+        lim = min(L, r_max)
+        best = 0
+        for h in range(H):
+            r_h = lim
+            acc = 0
+            for r in range(0, lim + 1):
+                if r > 0:
+                    acc += qg[e - r][h]
+                if acc <= thr:
+                    r_h = r
+                    break
+            best = max(best, r_h)
+        out.append(max(min(r_min, L), min(best, min(r_max, L))))
+    return np.asarray(out, dtype=np.int64)
