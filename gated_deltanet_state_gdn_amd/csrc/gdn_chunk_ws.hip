@@ -45,6 +45,7 @@
 // fragment whose contraction indices follow the accumulator rows lets a D tile be
 // used directly as a B operand (S in K S, Z/U in the solve, U in K^T U) and, read
 // the other way, as an A operand (S^T in S^T Q^T, U^T in U^T P^T).
+#include <atomic>
 #include <type_traits>
 
 #include "gdn_common.h"
@@ -510,19 +511,41 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
     int lane = lane0, lr = lane & 15, lg = lane >> 4;
     const bool is_state = wave < NSW;
 
-    // ---- block -> (sequence, v-head, column block); XCD-aware: consecutive logical
-    // blocks (the v-heads of one q/k head, the heads of one sequence) share an XCD's L2.
+    // ---- block -> work unit (sequence, v-head, column block) and its column slice.
+    // Blocks [0, n_full) take whole units.  The units that would leave the last round
+    // of the grid partly empty are instead split by columns into 2^split slices, one
+    // block each (the columns of S evolve independently; each slice repeats the
+    // unit's prep work), so that round fills more of the chip.  Within each range the
+    // order is XCD-aware: consecutive logical blocks (the slices of a unit, the v-heads
+    // of one q/k head, the heads of one sequence) share an XCD's L2.
     const int64_t nblk = (int64_t)gridDim.x;
-    int64_t bid = blockIdx.x;
-    if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-    const int cb = (int)(bid % NCB);
-    const int h = (int)((bid / NCB) % a.h_v);
-    const int n = (int)(bid / ((int64_t)NCB * a.h_v));
+    int64_t unit;
+    int slice = 0;
+    int ncols = W;                         // columns of this block
+    {
+        int64_t b = blockIdx.x;
+        if (b < a.n_full) {
+            if ((a.n_full & 7) == 0) b = (b & 7) * (a.n_full >> 3) + (b >> 3);
+            unit = b;
+        } else {
+            const int64_t m = nblk - a.n_full;
+            b -= a.n_full;
+            if ((m & 7) == 0) b = (b & 7) * (m >> 3) + (b >> 3);
+            unit = a.n_full + (b >> a.split);
+            slice = (int)(b & ((1 << a.split) - 1));
+            ncols = W >> a.split;
+        }
+    }
+    const int cb = (int)(unit % NCB);
+    const int h = (int)((unit / NCB) % a.h_v);
+    const int n = (int)(unit / ((int64_t)NCB * a.h_v));
+    const int c_lo = cb * W + slice * ncols;            // first d_v column of the block
+    const int nact = ncols / 16;                        // state waves with columns
     const int hk = (int)(((int64_t)h * a.h_qk) / a.h_v);
     const bool replay = a.r != nullptr;
 
     // ---- window selection (validates the device-resident cu_seqlens / r)
-    if (bid == 0) {
+    if (blockIdx.x == 0) {
         int bad = 0;
         for (int m = tid; m < a.n_seqs; m += NTHR) {
             const int64_t b0 = a.cu[m], b1 = a.cu[m + 1];
@@ -568,7 +591,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
     __syncthreads();
     const int64_t orow0 = gMisc[0];
     if (orow0 < 0 || orow0 + rn > (replay ? a.total_out : a.total_tokens)) return;
-    if (a.cu_out && h == 0 && cb == 0 && tid == 0) {
+    if (a.cu_out && h == 0 && c_lo == 0 && tid == 0) {
         a.cu_out[n] = (int32_t)orow0;
         if (n == a.n_seqs - 1) a.cu_out[n + 1] = (int32_t)(orow0 + rn);
     }
@@ -579,10 +602,14 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
     const E *vg = reinterpret_cast<const E *>(a.v);
     const int64_t sbase = ((int64_t)n * a.h_v + h) * DK * DV;
 
-    if (is_state) {
+    if (is_state && wave >= nact) {
+        // a state wave without columns (a split block): only the state waves' barriers
+        sync_lds();
+        for (int64_t c = 0; c < nch; ++c) sync_lds();
+    } else if (is_state) {
         // =====================================================================
         // state waves
-        const int col0 = cb * W + wave * 16;       // first d_v column of this wave
+        const int col0 = c_lo + wave * 16;         // first d_v column of this wave
         f32x4 S[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -912,11 +939,48 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
     }
 }
 
+// Workgroups of this kernel instance that can be resident at once on the current
+// device (compute units x blocks per unit), queried once per device.
 template <int DK, int DV, int W, class P, bool WITH_O>
-hipError_t launch_t(const ChunkArgs &a, hipStream_t stream)
+int64_t resident_slots()
 {
-    const int64_t nblk = (int64_t)a.n_seqs * a.h_v * (DV / W);
-    if (nblk <= 0) return hipSuccess;
+    static std::atomic<int64_t> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int64_t v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per, reinterpret_cast<const void *>(&gdn_chunk_ws_kernel<DK, DV, W, P, WITH_O>),
+            64 * (W / 16 + NPW), 0) != hipSuccess)
+        return 0;
+    v = (int64_t)cus * (per > 0 ? per : 1);
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+template <int DK, int DV, int W, class P, bool WITH_O>
+hipError_t launch_t(const ChunkArgs &a0, hipStream_t stream)
+{
+    const int64_t units = (int64_t)a0.n_seqs * a0.h_v * (DV / W);
+    if (units <= 0) return hipSuccess;
+    // split the units of a partial last round into column slices (2^split each, at least
+    // 16 columns) while they still fit in one round
+    ChunkArgs a = a0;
+    a.n_full = units;
+    a.split = 0;
+    const int64_t slots = resident_slots<DK, DV, W, P, WITH_O>();
+    if (slots > 0) {
+        const int64_t rem = units % slots;
+        int sp = 0;
+        while (rem > 0 && (16 << (sp + 1)) <= W && rem * (int64_t(2) << sp) <= slots) ++sp;
+        if (sp > 0) {
+            a.n_full = units - rem;
+            a.split = sp;
+        }
+    }
+    const int64_t nblk = a.n_full + ((units - a.n_full) << a.split);
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((gdn_chunk_ws_kernel<DK, DV, W, P, WITH_O>), dim3((unsigned)nblk),
                        dim3(64 * (W / 16 + NPW)), 0, stream, a);

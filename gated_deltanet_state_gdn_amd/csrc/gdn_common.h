@@ -23,6 +23,10 @@ struct ChunkArgs {
     int32_t n_seqs, h_qk, h_v;
     int32_t o_f32;              // o stored as fp32 (1) or in the input dtype (0)
     float scale;
+    // grid plan (set by the launcher): blocks [0, n_full) take whole work units, the
+    // rest take 1/2^split of a unit's columns each
+    int64_t n_full;
+    int32_t split;
 };
 
 // Launch the chunk kernel (state waves and prep waves on double-buffered LDS) for the

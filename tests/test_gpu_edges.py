@@ -200,3 +200,24 @@ def test_device_status_reports_bad_device_inputs():
     gdn.gdn_replay(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], short_out,
                    total_out_tokens=40, ws=ws)
     assert gdn.gdn_device_status(ws) == 8
+
+
+def test_column_slices_are_bitwise_equal_to_whole_units():
+    # 36 layers x 32 v-heads = 1152 units: 1024 whole-unit blocks plus the last 128 units
+    # in two column slices each; one layer per call: every unit in eight slices.
+    import gated_deltanet_state_gdn_amd as gdn
+    w = W.small(W.config(2), L=[300], r=[130], layers=36)
+    inp = W.make_inputs(w, device="cuda")
+    say("case column slices vs whole units, 36 layers")
+    tot = int(inp["r_host"].sum())
+    S_all, o_all, _ = gdn.gdn_replay(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                     inp["cu_seqlens"], inp["r"], total_out_tokens=tot)
+    for layer in (0, 17, 35):
+        sl = slice(300 * layer, 300 * (layer + 1))
+        cu1 = torch.tensor([0, 300], dtype=torch.int32, device="cuda")
+        r1 = inp["r"][layer:layer + 1].contiguous()
+        S1, o1, _ = gdn.gdn_replay(inp["q"][sl], inp["k"][sl], inp["v"][sl], inp["g"][sl],
+                                   inp["beta"][sl], cu1, r1, total_out_tokens=130)
+        torch.cuda.synchronize()
+        assert torch.equal(S1[0], S_all[layer])
+        assert torch.equal(o1.view(torch.int16), o_all[130 * layer:130 * (layer + 1)].view(torch.int16))
