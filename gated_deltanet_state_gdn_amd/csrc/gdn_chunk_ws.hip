@@ -137,12 +137,17 @@ __device__ __forceinline__ float v_at(typename Raw<P>::T v) {
 // that pair with accumulator rows 4g + i of two 16-row tiles; an aligned group of four
 // columns is always 8 contiguous bytes.  fp32 keeps the natural order (logical chunk
 // 4 kb + g = columns 16 kb + 4g .. 4g+3).
-// The swizzle (swap of the two 2-bit halves of the row index for 256-byte rows) keeps
-// both access patterns free of bank conflicts: 16-byte row fragments (16 rows, one
-// logical chunk) and the 8-byte transposing reads of K^T fragments (4 rows x 4 chunks).
+// The swizzle for 256-byte rows puts the three low row bits, reversed, on chunk bits
+// 3..1.  Chosen by measurement (the LDS bank-conflict counter over every XOR swizzle of
+// the low four row bits): it is free of conflicts for 16-byte row fragments (16 rows,
+// one logical chunk per 16 lanes) and keeps the 8-byte transposing reads of K^T
+// fragments (4 rows x 4 chunks) at the rate of an unswizzled 8-byte read; swapping the
+// two 2-bit halves of the row index, the obvious choice, doubles the fragment reads'
+// cost.  128-byte rows keep a swap-style swizzle.
 template <int RB>
 __device__ __forceinline__ int swz(int r) {
-    return RB == 256 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+    return RB == 256 ? (((r & 1) << 3) | ((r & 2) << 1) | ((r & 4) >> 1))
+                     : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 template <int RB>
 __device__ __forceinline__ int chunk_at(int r, int c) { return r * RB + 16 * (c ^ swz<RB>(r)); }
@@ -883,15 +888,23 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
 #pragma unroll
                 for (int j = 0; j < NR; ++j) {
                     if constexpr (P::kBF16) {
+                        // a unit is logical chunks c0 and c0 + 1 of a row; the lanes of the
+                        // upper half of a row write them in the other order, so that each
+                        // store's eight lanes of one row hit eight distinct 16-byte slots
+                        // modulo 128 bytes (the stores' bank rule)
                         const int c0 = 4 * (pu >> 1) + 2 * (pu & 1);
-                        const int o0 = chunk_at<RBK>(row + RPJ * j, c0), o1 = chunk_at<RBK>(row + RPJ * j, c0 + 1);
+                        const bool sw = (pu & 4) != 0;
+                        const int oa = chunk_at<RBK>(row + RPJ * j, sw ? c0 + 1 : c0);
+                        const int ob = chunk_at<RBK>(row + RPJ * j, sw ? c0 : c0 + 1);
                         const u32x4 a0 = kpf[2 * j], a1 = kpf[2 * j + 1];
-                        *reinterpret_cast<u32x4 *>(Ks + o0) = u32x4{a0.x, a0.y, a1.x, a1.y};
-                        *reinterpret_cast<u32x4 *>(Ks + o1) = u32x4{a0.z, a0.w, a1.z, a1.w};
+                        const u32x4 k0 = {a0.x, a0.y, a1.x, a1.y}, k1 = {a0.z, a0.w, a1.z, a1.w};
+                        *reinterpret_cast<u32x4 *>(Ks + oa) = sw ? k1 : k0;
+                        *reinterpret_cast<u32x4 *>(Ks + ob) = sw ? k0 : k1;
                         if (WITH_O) {
                             const u32x4 b0 = qpf[2 * j], b1 = qpf[2 * j + 1];
-                            *reinterpret_cast<u32x4 *>(Qs + o0) = u32x4{b0.x, b0.y, b1.x, b1.y};
-                            *reinterpret_cast<u32x4 *>(Qs + o1) = u32x4{b0.z, b0.w, b1.z, b1.w};
+                            const u32x4 q0 = {b0.x, b0.y, b1.x, b1.y}, q1 = {b0.z, b0.w, b1.z, b1.w};
+                            *reinterpret_cast<u32x4 *>(Qs + oa) = sw ? q1 : q0;
+                            *reinterpret_cast<u32x4 *>(Qs + ob) = sw ? q0 : q1;
                         }
                     } else {
                         const int o = chunk_at<RBK>(row + RPJ * j, pu);
