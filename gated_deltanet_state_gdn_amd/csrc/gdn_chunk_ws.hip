@@ -277,8 +277,11 @@ struct Lds {
     static constexpr int TILE = 256 * (int)sizeof(E);          // one 16x16 tile
     static constexpr int NTA = P::kBF16 ? 6 : 10;              // tile pairs (bf16) / tiles (fp32)
     static constexpr int UNIT = P::kBF16 ? 1024 : TILE;
-    static constexpr int oGate = 0;                            // H, e, b, G_last, scale e, rho
-    static constexpr int oK = 6 * CH * 4;
+    // gate rows: H, e sig, b, G_last / sig, scale e sig, rho (int), then the chunk's
+    // state-scale words (renormalisation factor, sig after the chunk); 8 rows keep K at a
+    // 1 KB boundary
+    static constexpr int oGate = 0;
+    static constexpr int oK = 8 * CH * 4;
     static constexpr int oQ = oK + CH * RBK;
     static constexpr int oA = oQ + (WITH_O ? CH * RBK : 0);     // -A
     static constexpr int oT = oA + NTA * UNIT;                   // 4 tiles T_bb - I
@@ -778,9 +781,15 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                 }
             }
 
-            // S <- e_last S + K^T diag(G_last) U
+            // S <- e_last S + K^T diag(G_last) U, on the stored state S~ = S / sig: the
+            // gate rows carry e sig_{c-1} and G_last / sig_c, so the decay costs nothing
+            // here except on the rare chunks that renormalise S~ (factor != 1)
             {
-                const float gam_c = gE[CH - 1];
+                const float rn = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(gH[6 * CH])));
+                if (rn != 1.f) {
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) S[rt] *= rn;
+                }
                 Frag dh[KBT], dl[KBT];
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
@@ -795,7 +804,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                 }
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
-                    f32x4 s = S[rt] * gam_c;
+                    f32x4 s = S[rt];
 #pragma unroll
                     for (int kb = 0; kb < KBT; ++kb) {
                         if constexpr (P::kBF16) {
@@ -812,12 +821,15 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             sync_lds();   // this chunk's buffer is free; the next one is prepared
         }
 
-        // ---- state write-back
+        // ---- state write-back: S = sig S~, sig from the last chunk's gate rows
+        const float sig = nch > 0 ? reinterpret_cast<const float *>(smem + ((nch - 1) & 1) * L::BUF +
+                                                                    L::oGate)[6 * CH + 1]
+                                  : 1.f;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                a.S_out[sbase + (int64_t)(16 * rt + 4 * lg + i) * DV + col0 + lr] = S[rt][i];
+                a.S_out[sbase + (int64_t)(16 * rt + 4 * lg + i) * DV + col0 + lr] = S[rt][i] * sig;
     } else {
         // =====================================================================
         // prep waves: chunk c + 1's operands while the state waves process chunk c
@@ -838,6 +850,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         u32x4 kpf[NR * VPU], qpf[NR * VPU];
         uint32_t gpf = 0, bpf = 0;
         Gates gt = {0.f, 0.f, 0.f, 0.f, -1};
+        float sig = 1.f;                           // scale of the stored state (gate wave)
         constexpr int GW = NPW - 1;                // the wave that owns the gates
         // the chunk starting at token cc of the window into registers (rows past the
         // window read as 0: g = b = 0 there; a chunk past the window reads nothing)
@@ -914,13 +927,26 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                 }
             }
             if (pw == GW) {
+                // the state waves keep S~ = S / sig: the chunk's decay e_last goes into sig,
+                // and into S~ (factor rn) only when sig would drop below 2^-60 or the chunk
+                // holds a reset (e_last = 0); then sig restarts at 1
+                const float el = __shfl(gt.e, 63);
+                const float cand = el * sig;
+                const bool renorm = !(cand >= 0x1p-60f);
+                const float rn = renorm ? cand : 1.f;
+                const float sig_new = renorm ? 1.f : cand;
                 float *gH = reinterpret_cast<float *>(buf + L::oGate);
                 gH[lane] = gt.h;
-                gH[CH + lane] = gt.e;
+                gH[CH + lane] = gt.e * sig;
                 gH[2 * CH + lane] = gt.b;
-                gH[3 * CH + lane] = gt.l;
-                gH[4 * CH + lane] = a.scale * gt.e;
+                gH[3 * CH + lane] = gt.l / sig_new;
+                gH[4 * CH + lane] = a.scale * (gt.e * sig);
                 reinterpret_cast<int *>(gH + 5 * CH)[lane] = gt.rho;
+                if (lane == 0) {
+                    gH[6 * CH] = rn;
+                    gH[6 * CH + 1] = sig_new;
+                }
+                sig = sig_new;
             }
             fetch((cc + 1) * CH);
             prep_sync(pctr, target, lane, pfail);
