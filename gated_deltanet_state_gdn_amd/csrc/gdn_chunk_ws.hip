@@ -277,7 +277,7 @@ struct Lds {
     static constexpr int TILE = 256 * (int)sizeof(E);          // one 16x16 tile
     static constexpr int NTA = P::kBF16 ? 6 : 10;              // tile pairs (bf16) / tiles (fp32)
     static constexpr int UNIT = P::kBF16 ? 1024 : TILE;
-    // gate rows: H, e sig, b, G_last / sig, scale e sig, rho (int), then the chunk's
+    // gate rows: H log2(e), e sig, b, G_last / sig, scale e sig, rho (int), then the chunk's
     // state-scale words (renormalisation factor, sig after the chunk); 8 rows keep K at a
     // 1 KB boundary
     static constexpr int oGate = 0;
@@ -381,10 +381,13 @@ __device__ __forceinline__ f32x4 tile_store(char *buf, float hr, float br, int r
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int c = 16 * tj + 4 * lg + e;
-        // exp of every entry, then a select: no divergent branch (the unused ones may be inf)
-        const float ex = __expf(hr - hc[e]);
-        const float gam = (c <= rr && rho <= c) ? ex : 0.f;
-        av[e] = c < rr ? -br * gam * kk[e] : 0.f;
+        // 2^(H_i - H_j) with H in units of log2(e), of every entry, then a select: no
+        // divergent branch (the unused ones may be inf).  Off-diagonal tiles (ti > tj,
+        // known when inlined) lie wholly below the diagonal.
+        const float ex = __builtin_amdgcn_exp2f(hr - hc[e]);
+        const bool below = ti > tj;
+        const float gam = ((below || c <= rr) && rho <= c) ? ex : 0.f;
+        av[e] = (below || c < rr) ? -br * gam * kk[e] : 0.f;
         pv[e] = scale * gam * qk[e];
     }
     if constexpr (P::kBF16) {
@@ -936,7 +939,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                 const float rn = renorm ? cand : 1.f;
                 const float sig_new = renorm ? 1.f : cand;
                 float *gH = reinterpret_cast<float *>(buf + L::oGate);
-                gH[lane] = gt.h;
+                gH[lane] = gt.h * 1.4426950408889634f;   // log2(e)
                 gH[CH + lane] = gt.e * sig;
                 gH[2 * CH + lane] = gt.b;
                 gH[3 * CH + lane] = gt.l / sig_new;
