@@ -759,7 +759,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                         }
                     }
                 }
-                if (a.o_out) {
+                {   // (the launcher instantiates WITH_O only for a non-null o_out)
                     // rows past the window end fall outside the buffer and are dropped
                     const int64_t orow_first = replay ? orow0 + c0 : wbeg + c0;
                     const bool f32o = !P::kBF16 || a.o_f32;
