@@ -58,6 +58,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-extra", action="store_true", help="skip prefill / per-layer timings")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the slow-decay replay-budget sweep")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -199,6 +200,8 @@ def main():
             out["suffix_prefill"] = suffix_leg(w, inp, gdn, stream, ws, pms / layers, n_seqs)
         out["adaptive_replay_len"] = adaptive_leg(w, inp, gdn, stream, ws, Sp, layers, with_o)
         out["transfer_overlap"] = overlap_leg(step, stream, kern_ms)
+        if not args.no_sweep:
+            out["gate_sweep"] = gate_sweep_leg(gdn, stream, with_o)
         del Sp
 
     if not args.no_cpu_baseline:
@@ -291,6 +294,40 @@ def adaptive_leg(w, inp, gdn, stream, ws, S_full, layers, with_o, eps=1e-3):
             "replay_us_per_layer": t_rep * 1e3 / layers,
             "relerr_vs_full": {"max": float(rel.max()), "median": float(rel.median()),
                                "nonfinite": int(nf.sum())}}
+
+
+def gate_sweep_leg(gdn, stream, with_o):
+    """Slow-decay layer (16 heads, d = 128, bf16, L = 32768, alpha ~ 0.9997), without and
+    with one alpha = 0 token per head: replay time and error against full prefill at the
+    replay budgets 1, 2, 5, 10 and 20 %, and the full prefill itself."""
+    import torch
+    import workloads as W
+    res = {}
+    for variant, resets in (("plain", False), ("reset", True)):
+        w = W.config(4).with_(reset_heads=resets)
+        inp = W.make_inputs(w, device=stream.device)
+        q, k, v, g, beta, cu = (inp[x] for x in ("q", "k", "v", "g", "beta", "cu_seqlens"))
+        L = int(w.lengths[0])
+        S_full, _ = gdn.gdn_prefill(q, k, v, g, beta, cu, o_out=None, stream=stream)
+        t_full = _time(lambda: gdn.gdn_prefill(q, k, v, g, beta, cu, S_out=S_full, o_out=None,
+                                               stream=stream), stream, 2)
+        rows = []
+        for rho in W.GATE_SWEEP:
+            rr = W.replay_len(L, rho)
+            r = torch.tensor([rr], dtype=torch.int32, device=q.device)
+            S = torch.empty_like(S_full)
+            o = torch.empty((rr, w.h_v, w.d_v), dtype=q.dtype, device=q.device) if with_o else None
+            fn = lambda: gdn.gdn_replay(q, k, v, g, beta, cu, r, total_out_tokens=rr, S_out=S,
+                                        o_out=o, stream=stream)
+            t = _time(fn, stream, 5)
+            rel, _ = gdn.gdn_state_relerr(S, S_full, stream=stream)
+            torch.cuda.synchronize()
+            rows.append({"budget": rho, "r": rr, "replay_us": t * 1e3,
+                         "replayed_tokens_per_s": rr / (t * 1e-3),
+                         "relerr_max": float(rel.max()), "relerr_median": float(rel.median())})
+        res[variant] = {"full_prefill_us": t_full * 1e3, "budgets": rows}
+        del inp
+    return res
 
 
 def overlap_leg(step, stream, replay_ms, fa_layers=12, kv_heads=2, head_dim=256, tokens=32768):
