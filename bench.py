@@ -156,6 +156,16 @@ def main():
     }
 
     if not args.no_extra:
+        # the same replay without per-token outputs, against its own algorithmic bytes
+        if with_o:
+            fs = lambda: gdn.gdn_replay(q, k, v, g, beta, cu, r, total_out_tokens=tot, S_out=S,
+                                        o_out=None, ws=ws, scale=w.scale, stream=stream)
+            ms_s = _time(fs, stream, 10)
+            ab_s = algorithmic_bytes(w, tot, n_seqs, False)
+            out["state_only"] = {"us_per_layer": ms_s * 1e3 / layers,
+                                 "replayed_tokens_per_s": tot / (ms_s * 1e-3),
+                                 "algorithmic_bytes_per_launch": ab_s,
+                                 "roofline_frac": ab_s / (ms_s * 1e-3) / 1e9 / HBM_PEAK_GBS}
         # one layer per call (latency of a single layer's rebuild)
         if w.layers > 1:
             per = int(inp["cu_host"][1])
