@@ -205,11 +205,14 @@ __device__ __forceinline__ bf16x8 frag_dt(const char *T, int pair, int lane) {
 // 16x16 tiles, row-major (32-byte rows in bf16, 64-byte rows in fp32): T_bb - I, and for
 // fp32 inputs also -A and P; lower tile (ti, tj) of a 64x64 matrix at ti*(ti+1)/2 + tj.
 __device__ __forceinline__ int tri_index(int ti, int tj) { return ti * (ti + 1) / 2 + tj; }
-// bf16 fragment with one half (4 contraction indices) from a tile and the other zero.
-__device__ __forceinline__ bf16x8 frag_half(const uint16_t *T, int tile, bool upper, int lane) {
-    const u32x2 a = *reinterpret_cast<const u32x2 *>(T + tile * 256 + (lane & 15) * 16 + 4 * (lane >> 4));
-    const u32x4 u = upper ? u32x4{0u, 0u, a.x, a.y} : u32x4{a.x, a.y, 0u, 0u};
-    return __builtin_bit_cast(bf16x8, u);
+// Operands of a 16x16x16 product (4 contraction indices per lane), for the products
+// whose other half would be zero: the first tile of a tile pair and a 16x16 tile, both
+// in the A-operand layout (lane l: row l%16, columns 4 (l/16) .. +3).
+__device__ __forceinline__ u32x2 frag_dt_first(const char *T, int pair, int lane) {
+    return *reinterpret_cast<const u32x2 *>(T + pair * 1024 + dt_at(lane & 15, lane >> 4));
+}
+__device__ __forceinline__ u32x2 frag_t16(const uint16_t *T, int tile, int lane) {
+    return *reinterpret_cast<const u32x2 *>(T + tile * 256 + (lane & 15) * 16 + 4 * (lane >> 4));
 }
 __device__ __forceinline__ f32x4 frag_tile(const float *T, int tile, int lane) {
     return *reinterpret_cast<const f32x4 *>(T + tile * 256 + (lane & 15) * 16 + 4 * (lane >> 4));
@@ -221,6 +224,14 @@ __device__ __forceinline__ bf16x8 bfrag_hi(const f32x4 &t0, const f32x4 &t1) {
     const u32x4 u = {pk_bf16(t0[0], t0[1]), pk_bf16(t0[2], t0[3]), pk_bf16(t1[0], t1[1]),
                      pk_bf16(t1[2], t1[3])};
     return __builtin_bit_cast(bf16x8, u);
+}
+// One accumulator tile (16 contraction rows) as the B operand of a 16x16x16 product.
+__device__ __forceinline__ u32x2 bfrag16(const f32x4 &t) {
+    return u32x2{pk_bf16(t[0], t[1]), pk_bf16(t[2], t[3])};
+}
+__device__ __forceinline__ f32x4 mma16(f32x4 c, u32x2 a, u32x2 b) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
 }
 __device__ __forceinline__ void bfrag_split(const f32x4 &t0, const f32x4 &t1, bf16x8 &hi,
                                             bf16x8 &lo) {
@@ -642,12 +653,16 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             const int64_t ln = (rn - cc) < CH ? (rn - cc) : CH;
             const Rsrc rs = make_rsrc(vg + ((wbeg + cc) * a.h_v + h) * (int64_t)DV + col0,
                                       ln * (int64_t)vrow);
-            const uint32_t vo = (uint32_t)(4 * (lane >> 4)) * vrow + (uint32_t)(lane & 15) * (uint32_t)sizeof(E);
+            // token rows 16 tt + 4 (lane/16) + i: one running offset, one add per load
+            uint32_t vo = (uint32_t)(4 * (lane >> 4)) * vrow + (uint32_t)(lane & 15) * (uint32_t)sizeof(E);
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    vreg[tt][i] = load_e<P>(rs, vo + (uint32_t)(16 * tt + i) * vrow);
+                for (int i = 0; i < 4; ++i) {
+                    vreg[tt][i] = load_e<P>(rs, vo);
+                    vo += (i == 3 ? 13u : 1u) * vrow;
+                    asm volatile("" : "+v"(vo));   // kept as a chain, not re-derived per load
+                }
         };
         // the initial state is in registers before the loop, so no wait for it is left
         // inside the loop (vmcnt(0) only; expcnt and lgkmcnt at their maxima)
@@ -706,16 +721,14 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             if constexpr (P::kBF16) {
                 const char *Ad = buf + L::oA;
                 const uint16_t *Tt = reinterpret_cast<const uint16_t *>(buf + L::oT);
-                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                // tiles (b, j < b): a 16x32 pair where both blocks exist, else a 16x16 product
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     f32x4 z = X[b];
-                    if (b >= 1) {   // tiles (b, 0), (b, 1); U_1 is still zero when b = 1
-                        z = mma(z, frag_dt(Ad, dt_index(b, 0), lane), bfrag_hi(U[0], b >= 2 ? U[1] : zero));
-                        if (b == 3) z = mma(z, frag_dt(Ad, dt_index(3, 1), lane), bfrag_hi(U[2], zero));
-                    }
-                    const bool odd = (b & 1) != 0;
-                    U[b] = mma(z, frag_half(Tt, b, odd, lane), odd ? bfrag_hi(zero, z) : bfrag_hi(z, zero));
+                    if (b == 1) z = mma16(z, frag_dt_first(Ad, dt_index(1, 0), lane), bfrag16(U[0]));
+                    if (b >= 2) z = mma(z, frag_dt(Ad, dt_index(b, 0), lane), bfrag_hi(U[0], U[1]));
+                    if (b == 3) z = mma16(z, frag_dt_first(Ad, dt_index(3, 1), lane), bfrag16(U[2]));
+                    U[b] = mma16(z, frag_t16(Tt, b, lane), bfrag16(z));
                 }
             } else {
                 const float *At = reinterpret_cast<const float *>(buf + L::oA);
