@@ -22,9 +22,11 @@
 //     because (I - b k k^T) acts on the d_k side only, so they exchange nothing.
 //     The outputs are formed transposed (O^T = S^T Q^T + U^T P^T), which puts four
 //     consecutive d_v entries of one token in a lane: one vector store per 16 tokens.
-//   * four prep waves: everything that does not depend on S, one chunk ahead -- the
-//     chunk's K and Q in LDS, the gate scan, the Gram products forming -A and
-//     P, and the diagonal-block inverses.
+//   * eight prep waves: everything that does not depend on S, one chunk ahead -- the
+//     chunk's K and Q in LDS (all eight), the Gram products forming -A and P and the
+//     diagonal-block inverses (seven), the gate scan (one).
+// The state waves keep S / sig instead of S, sig being the product of the chunk decays
+// since the last renormalisation, so the per-chunk decay e_last costs no pass over S.
 // One workgroup barrier per chunk hands a prepared buffer to the state waves; the
 // prep waves order their own steps with a counter in LDS.
 //
@@ -64,10 +66,6 @@ typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int CH = 64;       // chunk length (tokens)
 constexpr int NPW = 8;       // prep waves per workgroup
 
-__device__ __forceinline__ uint16_t f2bf(float f) {
-    __bf16 h = (__bf16)f;                  // round to nearest even (v_cvt_pk_bf16_f32)
-    return __builtin_bit_cast(uint16_t, h);
-}
 // Two floats to a bf16 pair (round to nearest even), the first in the low half.
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
@@ -239,16 +237,6 @@ __device__ __forceinline__ void bfrag_split(const f32x4 &t0, const f32x4 &t1, bf
     const u32x2 c = split2(t1[0], t1[1]), d = split2(t1[2], t1[3]);
     hi = __builtin_bit_cast(bf16x8, u32x4{a.x, b.x, c.x, d.x});
     lo = __builtin_bit_cast(bf16x8, u32x4{a.y, b.y, c.y, d.y});
-}
-
-__device__ __forceinline__ void st_e(float *p, float x) { *p = x; }
-__device__ __forceinline__ void st_e(uint16_t *p, float x) { *p = f2bf(x); }
-
-// Lower-triangular 16x16 tile list of a 64x64 product (ti >= tj).
-__device__ __forceinline__ void tri_tile(int idx, int &ti, int &tj) {
-    // 0:(0,0) 1:(1,0) 2:(1,1) 3:(2,0) 4:(2,1) 5:(2,2) 6:(3,0) 7:(3,1) 8:(3,2) 9:(3,3)
-    ti = idx >= 6 ? 3 : idx >= 3 ? 2 : idx >= 1 ? 1 : 0;
-    tj = idx - (ti * (ti + 1)) / 2;
 }
 
 // Workgroup barrier that orders LDS only: global loads stay in flight across it
@@ -868,12 +856,29 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         Gates gt = {0.f, 0.f, 0.f, 0.f, -1};
         float sig = 1.f;                           // scale of the stored state (gate wave)
         constexpr int GW = NPW - 1;                // the wave that owns the gates
+        // this lane's staging unit, the same in every chunk: its offset in a chunk's K / Q
+        // rows and its LDS slots (a bf16 unit is logical chunks c0 and c0 + 1 of a row; the
+        // lanes of the upper half of a row write them in the other order, so that each
+        // store's eight lanes of one row hit eight distinct 16-byte slots modulo 128 bytes,
+        // the stores' bank rule)
+        const int spt = 64 * pw + lane0;
+        const bool s_act = UT >= TH || spt < UT;   // with fewer units than threads, the last waves idle
+        const int spu = spt % NPU, srow = spt / NPU;
+        const uint32_t s_vo = (uint32_t)srow * krow +
+                              (uint32_t)(P::kBF16 ? 64 * (spu >> 1) + 16 * (spu & 1) : 16 * spu);
+        const bool s_sw = P::kBF16 && (spu & 4) != 0;
+        int s_oa[NR], s_ob[NR];
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+            const int c0 = P::kBF16 ? 4 * (spu >> 1) + 2 * (spu & 1) : spu;
+            s_oa[j] = chunk_at<RBK>(srow + RPJ * j, s_sw ? c0 + 1 : c0);
+            s_ob[j] = chunk_at<RBK>(srow + RPJ * j, s_sw ? c0 : c0 + 1);
+        }
         // the chunk starting at token cc of the window into registers (rows past the
         // window read as 0: g = b = 0 there; a chunk past the window reads nothing)
         auto fetch = [&](int64_t cc) {
             int lane = lane0;
             asm volatile("" : "+v"(lane));
-            const int pt = 64 * pw + lane;
             const int64_t ln = (rn - cc) < CH ? (rn - cc) : CH;
             const int64_t t0 = wbeg + cc;
             if (pw == GW) {   // first, so that waiting for them waits for nothing else
@@ -885,15 +890,12 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             const int64_t koff = (t0 * a.h_qk + hk) * (int64_t)DK;
             const Rsrc rk = make_rsrc(kg + koff, ln * (int64_t)krow);
             const Rsrc rq = make_rsrc(qg + koff, ln * (int64_t)krow);
-            const int pu = pt % NPU;
-            const uint32_t vo = (uint32_t)(pt / NPU) * krow +
-                                (uint32_t)(P::kBF16 ? 64 * (pu >> 1) + 16 * (pu & 1) : 16 * pu);
-            if (UT >= TH || pt < UT) {   // with fewer units than threads, the last waves idle
+            if (s_act) {
 #pragma unroll
                 for (int j = 0; j < NR; ++j)
 #pragma unroll
                     for (int v = 0; v < VPU; ++v) {
-                        const uint32_t o = vo + (uint32_t)(RPJ * j) * krow + 32u * v;
+                        const uint32_t o = s_vo + (uint32_t)(RPJ * j) * krow + 32u * v;
                         kpf[VPU * j + v] = __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0);
                         if (WITH_O) qpf[VPU * j + v] = __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0);
                     }
@@ -908,23 +910,15 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         auto prep = [&](int64_t cc) {
             int lane = lane0;
             asm volatile("" : "+v"(lane));
-            const int pt = 64 * pw + lane;
             char *buf = smem + (cc & 1) * L::BUF;
             char *Ks = buf + L::oK;
             char *Qs = buf + L::oQ;
-            if (UT >= TH || pt < UT) {
-                const int pu = pt % NPU, row = pt / NPU;
+            if (s_act) {
 #pragma unroll
                 for (int j = 0; j < NR; ++j) {
                     if constexpr (P::kBF16) {
-                        // a unit is logical chunks c0 and c0 + 1 of a row; the lanes of the
-                        // upper half of a row write them in the other order, so that each
-                        // store's eight lanes of one row hit eight distinct 16-byte slots
-                        // modulo 128 bytes (the stores' bank rule)
-                        const int c0 = 4 * (pu >> 1) + 2 * (pu & 1);
-                        const bool sw = (pu & 4) != 0;
-                        const int oa = chunk_at<RBK>(row + RPJ * j, sw ? c0 + 1 : c0);
-                        const int ob = chunk_at<RBK>(row + RPJ * j, sw ? c0 : c0 + 1);
+                        const bool sw = s_sw;
+                        const int oa = s_oa[j], ob = s_ob[j];
                         const u32x4 a0 = kpf[2 * j], a1 = kpf[2 * j + 1];
                         const u32x4 k0 = {a0.x, a0.y, a1.x, a1.y}, k1 = {a0.z, a0.w, a1.z, a1.w};
                         *reinterpret_cast<u32x4 *>(Ks + oa) = sw ? k1 : k0;
@@ -936,7 +930,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                             *reinterpret_cast<u32x4 *>(Qs + ob) = sw ? q0 : q1;
                         }
                     } else {
-                        const int o = chunk_at<RBK>(row + RPJ * j, pu);
+                        const int o = s_oa[j];
                         *reinterpret_cast<u32x4 *>(Ks + o) = kpf[j];
                         if (WITH_O) *reinterpret_cast<u32x4 *>(Qs + o) = qpf[j];
                     }
