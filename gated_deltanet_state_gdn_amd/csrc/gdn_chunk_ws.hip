@@ -709,13 +709,19 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             if constexpr (P::kBF16) {
                 const char *Ad = buf + L::oA;
                 const uint16_t *Tt = reinterpret_cast<const uint16_t *>(buf + L::oT);
-                // tiles (b, j < b): a 16x32 pair where both blocks exist, else a 16x16 product
+                // tiles (b, j < b): a 16x32 pair, or a 16x16 product when only tile (1, 0)
+                // exists.  A 16x16x16 product only ever accumulates onto values a vector
+                // instruction has read or written since the last matrix product (X after Y,
+                // z after its conversion to bf16): a 16x16x16 product that accumulates
+                // directly onto a 16x16x32 result gave wrong results, so (3, 2) stays a
+                // zero-padded 16x32 product in the 16x32 chain.
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     f32x4 z = X[b];
                     if (b == 1) z = mma16(z, frag_dt_first(Ad, dt_index(1, 0), lane), bfrag16(U[0]));
                     if (b >= 2) z = mma(z, frag_dt(Ad, dt_index(b, 0), lane), bfrag_hi(U[0], U[1]));
-                    if (b == 3) z = mma16(z, frag_dt_first(Ad, dt_index(3, 1), lane), bfrag16(U[2]));
+                    if (b == 3) z = mma(z, frag_dt(Ad, dt_index(3, 1), lane), bfrag_hi(U[2], zero));
                     U[b] = mma16(z, frag_t16(Tt, b, lane), bfrag16(z));
                 }
             } else {
