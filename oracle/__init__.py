@@ -11,7 +11,8 @@ token).  This wrapper only widens inputs exactly to float64 and passes pointers.
 walk back from the last token, sum the rounded log-gates, stop at the first window
 whose sum is at or below the threshold).
 
-Pins (see ``tests/test_oracle_pins.py``): explicit-matrix brute force, exact
+Pins (see ``tests/test_oracle_pins.py`` and ``tests/test_oracle_golden.py``): a worked
+example derived by hand (``tests/golden/``), explicit-matrix brute force, exact
 rational arithmetic, closed forms (alpha=1/beta=0, single token, orthonormal keys
 with beta=1, repeated key overwrite), and invariants (alpha=0 makes replay equal
 prefill, the attenuation bound, split-prefill composition, r=L and r=0, GVA as
