@@ -29,8 +29,10 @@
  * on `stream` (a hipStream_t; NULL = the null stream) except gdn_device_status.
  *
  * Ownership: the caller owns every buffer, including the workspace.  The compute
- * calls never allocate, free, synchronise or print, and keep no global mutable
- * state; calls are re-entrant given distinct workspaces.
+ * calls never allocate, free or synchronise; they print nothing unless the
+ * environment variable GDN_DEBUG is 1 (then a host-side rejection says why on
+ * stderr).  Their only global state is a per-device cache of the occupancy query
+ * (written once, atomically); calls are re-entrant given distinct workspaces.
  *
  * Errors: problems checkable on the host (null required pointer, bad dims,
  * h_v % h_qk != 0, unsupported d, misaligned pointer, small workspace) return a
