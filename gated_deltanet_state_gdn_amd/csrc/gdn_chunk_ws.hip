@@ -36,10 +36,14 @@
 // stores there).  Zero rows are inert: their g and b are 0, so they neither decay nor
 // write the state.
 //
-// Precision (bf16 inputs, fp32 state): q/k/v enter MFMA exactly; the gates, b and the
-// unit diagonal of the solve are applied in fp32; S enters Q S as hi + lo bf16 (hi in
-// K S); U enters P U and K^T U as hi + lo; P as hi + lo; A_bj, T_bb - I and Z as bf16.
-// fp32 inputs use fp32 MFMA throughout.
+// Precision (bf16 inputs, fp32 state): every matrix product has fp16 operands and fp32
+// accumulation.  q and k are converted to fp16 exactly when staged (they are L2-normalised,
+// so well inside fp16's range); S, U, P, A_bj, T_bb - I and Z are rounded to fp16 once
+// (11 significant bits against bf16's 8).  The bf16 layout this replaces needed hi + lo
+// pairs for S, U and P (1.7x the matrix products) and still left a 2-4x larger state
+// error, from the bf16 rounding of S in K S and of A_bj, T_bb - I and Z.  v, the gates, b
+// and the unit diagonal of the solve stay fp32.  Range: the stored state S / sig is kept within 64 |S| (sig >= 2^-6),
+// so state entries up to ~10^3 fit fp16.  fp32 inputs use fp32 MFMA throughout.
 //
 // Matrix-core layout used (16x16 MFMA): lane l supplies row l%16 of A and column
 // l%16 of B; element j of lane group l/16 in A pairs with element j of the same
@@ -57,8 +61,10 @@ namespace {
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 h16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 h16x4;
+typedef __attribute__((ext_vector_type(2))) _Float16 h16x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __amdgpu_buffer_rsrc_t Rsrc;
@@ -66,17 +72,21 @@ typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int CH = 64;       // chunk length (tokens)
 constexpr int NPW = 8;       // prep waves per workgroup
 
-// Two floats to a bf16 pair (round to nearest even), the first in the low half.
+// Two floats to a bf16 pair (round to nearest even), the first in the low half: the
+// outputs o of the bf16 path.
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
-__device__ __forceinline__ float lo_f(uint32_t p) { return __uint_as_float(p << 16); }
-__device__ __forceinline__ float hi_f(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
-// {hi, lo} with hi = bf16(x), lo = bf16(x - hi) for a pair: hi + lo carries 16
-// significant bits.
-__device__ __forceinline__ u32x2 split2(float a, float b) {
-    const uint32_t hi = pk_bf16(a, b);
-    return u32x2{hi, pk_bf16(a - lo_f(hi), b - hi_f(hi))};
+// Two floats to an fp16 pair (round to nearest even, v_cvt_pk_f16_f32), the first in the
+// low half: every matrix operand of the bf16 path.
+__device__ __forceinline__ uint32_t pk_h(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, h16x2));
+}
+// A bf16 pair as an fp16 pair: exact for magnitudes in [2^-14, 65504], the range the
+// L2-normalised q and k of a Gated DeltaNet layer live in (smaller ones round to fp16
+// subnormals).
+__device__ __forceinline__ uint32_t bf2_to_h2(uint32_t p) {
+    return pk_h(__uint_as_float(p << 16), __uint_as_float(p & 0xffff0000u));
 }
 
 // ---------------------------------------------------------------- policies
@@ -86,11 +96,13 @@ struct PolF32 {
     typedef float E;                 // element type of q/k/v and of LDS operands
     typedef f32x4 Frag;
 };
+// bf16 inputs: q, k, v stored as bf16; every matrix operand an fp16 value (q and k
+// converted exactly when staged, the fp32 intermediates rounded once), fp32 accumulation.
 struct PolBF16 {
     static constexpr bool kBF16 = true;
     static constexpr int KB = 32;
     typedef uint16_t E;
-    typedef bf16x8 Frag;
+    typedef h16x8 Frag;
 };
 
 __device__ __forceinline__ f32x4 mma(f32x4 c, f32x4 a, f32x4 b) {
@@ -100,8 +112,8 @@ __device__ __forceinline__ f32x4 mma(f32x4 c, f32x4 a, f32x4 b) {
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
     return c;
 }
-__device__ __forceinline__ f32x4 mma(f32x4 c, bf16x8 a, bf16x8 b) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mma(f32x4 c, h16x8 a, h16x8 b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------- global memory
@@ -165,7 +177,7 @@ __device__ __forceinline__ F frag_sw(const char *M, int r0, int kb, int lane) {
 // second half), columns 16 rt + 4 x .. +3.
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 template <int RB>
-__device__ __forceinline__ bf16x8 frag_kt(const char *K, int rt, int kb, int lane) {
+__device__ __forceinline__ h16x8 frag_kt(const char *K, int rt, int kb, int lane) {
     const int m = lane & 15;
     const int row = 32 * kb + 4 * (lane >> 4) + (m >> 2);
     const char *p = K + chunk_at<RB>(row, 4 * (rt >> 1) + (m & 3)) + 8 * (rt & 1);
@@ -173,7 +185,7 @@ __device__ __forceinline__ bf16x8 frag_kt(const char *K, int rt, int kb, int lan
     const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)p);
     const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(p + 16 * RB));
     const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
-    return __builtin_bit_cast(bf16x8, u32x4{ua.x, ua.y, ub.x, ub.y});
+    return __builtin_bit_cast(h16x8, u32x4{ua.x, ua.y, ub.x, ub.y});
 }
 // fp32 fragment of M^T (the rows of M are the contraction index): lane l gives column
 // c0 + l%16 and rows 16 kb + 4 (l/16) + i.
@@ -195,9 +207,9 @@ __device__ __forceinline__ f32x4 frag_cols_f32(const char *M, int c0, int kb, in
 // Pair index of (ti, kb), kb <= ti/2:  0:(0,0) 1:(1,0) 2:(2,0) 3:(2,1) 4:(3,0) 5:(3,1).
 __device__ __forceinline__ int dt_index(int ti, int kb) { return ti < 2 ? ti : 2 * ti - 2 + kb; }
 __device__ __forceinline__ int dt_at(int r, int g) { return r * 64 + 16 * (g ^ ((r >> 2) & 3)); }
-__device__ __forceinline__ bf16x8 frag_dt(const char *T, int pair, int lane) {
+__device__ __forceinline__ h16x8 frag_dt(const char *T, int pair, int lane) {
     return __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const u32x4 *>(T + pair * 1024 + dt_at(lane & 15, lane >> 4)));
+        h16x8, *reinterpret_cast<const u32x4 *>(T + pair * 1024 + dt_at(lane & 15, lane >> 4)));
 }
 
 // 16x16 tiles, row-major (32-byte rows in bf16, 64-byte rows in fp32): T_bb - I, and for
@@ -217,26 +229,18 @@ __device__ __forceinline__ f32x4 frag_tile(const float *T, int tile, int lane) {
 }
 
 // ---------------------------------------------------------------- register operands
-// Two accumulator tiles (16 contraction rows each) as one bf16 operand.
-__device__ __forceinline__ bf16x8 bfrag_hi(const f32x4 &t0, const f32x4 &t1) {
-    const u32x4 u = {pk_bf16(t0[0], t0[1]), pk_bf16(t0[2], t0[3]), pk_bf16(t1[0], t1[1]),
-                     pk_bf16(t1[2], t1[3])};
-    return __builtin_bit_cast(bf16x8, u);
+// Two accumulator tiles (16 contraction rows each) as one fp16 operand.
+__device__ __forceinline__ h16x8 bfrag(const f32x4 &t0, const f32x4 &t1) {
+    const u32x4 u = {pk_h(t0[0], t0[1]), pk_h(t0[2], t0[3]), pk_h(t1[0], t1[1]), pk_h(t1[2], t1[3])};
+    return __builtin_bit_cast(h16x8, u);
 }
 // One accumulator tile (16 contraction rows) as the B operand of a 16x16x16 product.
 __device__ __forceinline__ u32x2 bfrag16(const f32x4 &t) {
-    return u32x2{pk_bf16(t[0], t[1]), pk_bf16(t[2], t[3])};
+    return u32x2{pk_h(t[0], t[1]), pk_h(t[2], t[3])};
 }
 __device__ __forceinline__ f32x4 mma16(f32x4 c, u32x2 a, u32x2 b) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
-                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ void bfrag_split(const f32x4 &t0, const f32x4 &t1, bf16x8 &hi,
-                                            bf16x8 &lo) {
-    const u32x2 a = split2(t0[0], t0[1]), b = split2(t0[2], t0[3]);
-    const u32x2 c = split2(t1[0], t1[1]), d = split2(t1[2], t1[3]);
-    hi = __builtin_bit_cast(bf16x8, u32x4{a.x, b.x, c.x, d.x});
-    lo = __builtin_bit_cast(bf16x8, u32x4{a.y, b.y, c.y, d.y});
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h16x4, a),
+                                                 __builtin_bit_cast(h16x4, b), c, 0, 0, 0);
 }
 
 // Workgroup barrier that orders LDS only: global loads stay in flight across it
@@ -285,8 +289,7 @@ struct Lds {
     static constexpr int oA = oQ + (WITH_O ? CH * RBK : 0);     // -A
     static constexpr int oT = oA + NTA * UNIT;                   // 4 tiles T_bb - I
     static constexpr int oPh = oT + 4 * TILE;                    // P
-    static constexpr int oPl = oPh + (WITH_O ? NTA * UNIT : 0);  // bf16 low parts of P
-    static constexpr int BUF = oPl + ((WITH_O && P::kBF16) ? NTA * UNIT : 0);
+    static constexpr int BUF = oPh + (WITH_O ? NTA * UNIT : 0);
     static constexpr int oMisc = 2 * BUF;
     static constexpr int bytes = oMisc + 64;
 };
@@ -330,7 +333,7 @@ __device__ __forceinline__ Gates gate_scan(float gv, float bv, int lane) {
 // LDS latency of one tile with the work of the previous one:
 //   tile_load  every fragment and gate value the tile needs, issued together;
 //   tile_mma   K_tj K_ti^T and K_tj Q_ti^T on the matrix cores;
-//   tile_store -A and P = scale lower(Q K^T o G) (hi + lo for bf16) into LDS.
+//   tile_store -A and P = scale lower(Q K^T o G) (fp16 for bf16 inputs) into LDS.
 // The products are formed as K_tj K_ti^T and K_tj Q_ti^T, so that element e of lane l is
 //     kk[e] = k_{16 tj + 4 (l/16) + e} . k_{16 ti + l%16},
 //     qk[e] = k_{16 tj + 4 (l/16) + e} . q_{16 ti + l%16},
@@ -391,12 +394,9 @@ __device__ __forceinline__ f32x4 tile_store(char *buf, float hr, float br, int r
     }
     if constexpr (P::kBF16) {
         const int eo = dt_index(ti, tj >> 1) * 1024 + dt_at(lr, lg) + 8 * (tj & 1);
-        *reinterpret_cast<u32x2 *>(buf + L::oA + eo) = u32x2{pk_bf16(av[0], av[1]), pk_bf16(av[2], av[3])};
-        if constexpr (WITH_O) {
-            const u32x2 p01 = split2(pv[0], pv[1]), p23 = split2(pv[2], pv[3]);
-            *reinterpret_cast<u32x2 *>(buf + L::oPh + eo) = u32x2{p01.x, p23.x};
-            *reinterpret_cast<u32x2 *>(buf + L::oPl + eo) = u32x2{p01.y, p23.y};
-        }
+        *reinterpret_cast<u32x2 *>(buf + L::oA + eo) = u32x2{pk_h(av[0], av[1]), pk_h(av[2], av[3])};
+        if constexpr (WITH_O)
+            *reinterpret_cast<u32x2 *>(buf + L::oPh + eo) = u32x2{pk_h(pv[0], pv[1]), pk_h(pv[2], pv[3])};
     } else {
         const int eo = tri_index(ti, tj) * 256 + lr * 16 + 4 * lg;
         *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(buf + L::oA) + eo) = av;
@@ -411,13 +411,13 @@ __device__ __forceinline__ f32x4 tile_store(char *buf, float hr, float br, int r
 // Y in the accumulator layout (lane l: rows 4 (l/16) + i, column l%16); D comes out in the
 // accumulator layout.  Read the other way round, mm16(C, Y, X) gives C + X Y in the
 // A-operand layout.
-__device__ __forceinline__ i16x4 pk4(f32x4 x) {
-    return __builtin_bit_cast(i16x4, u32x2{pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3])});
+__device__ __forceinline__ h16x4 pk4(f32x4 x) {
+    return __builtin_bit_cast(h16x4, u32x2{pk_h(x[0], x[1]), pk_h(x[2], x[3])});
 }
 template <bool BF16>
 __device__ __forceinline__ f32x4 mm16(f32x4 c, f32x4 x, f32x4 y) {
     if constexpr (BF16) {
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pk4(x), pk4(y), c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(pk4(x), pk4(y), c, 0, 0, 0);
     } else {   // fp32 operands for fp32 inputs (four 16x16x4 steps)
 #pragma unroll
         for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(x[j], y[j], c, 0, 0, 0);
@@ -450,7 +450,7 @@ __device__ __forceinline__ void diag_inverse(f32x4 Nr, E *Tt, int lane) {
     const f32x4 Tm = Tr - I4;
     E *row = Tt + lr * 16 + 4 * lg;
     if constexpr (sizeof(E) == 2) {
-        *reinterpret_cast<u32x2 *>(row) = u32x2{pk_bf16(Tm[0], Tm[1]), pk_bf16(Tm[2], Tm[3])};
+        *reinterpret_cast<u32x2 *>(row) = u32x2{pk_h(Tm[0], Tm[1]), pk_h(Tm[2], Tm[3])};
     } else {
         *reinterpret_cast<f32x4 *>(row) = Tm;
     }
@@ -672,7 +672,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             const float *gH = reinterpret_cast<const float *>(buf + L::oGate);
             const float *gE = gH + CH, *gB = gE + CH, *gL = gB + CH, *gEs = gL + CH;
 
-            // X = K S (S as hi bf16) and (Q S)^T = S^T Q^T (S as hi + lo), by k-block
+            // X = K S and (Q S)^T = S^T Q^T, by k-block (S rounded once to the operand type)
             f32x4 X[4], OT[4];
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
@@ -681,8 +681,8 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             }
 #pragma unroll
             for (int kb = 0; kb < KBK; ++kb) {
-                Frag sh, sl;
-                if constexpr (P::kBF16) bfrag_split(S[2 * kb], S[2 * kb + 1], sh, sl);
+                Frag sh;
+                if constexpr (P::kBF16) sh = bfrag(S[2 * kb], S[2 * kb + 1]);
                 else sh = S[kb];
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
@@ -690,7 +690,6 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                     if constexpr (WITH_O) {
                         const Frag qf = frag_sw<RBK, Frag>(Qs, 16 * tt, kb, lane);
                         OT[tt] = mma(OT[tt], sh, qf);
-                        if constexpr (P::kBF16) OT[tt] = mma(OT[tt], sl, qf);
                     }
                 }
             }
@@ -720,8 +719,8 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                 for (int b = 0; b < 4; ++b) {
                     f32x4 z = X[b];
                     if (b == 1) z = mma16(z, frag_dt_first(Ad, dt_index(1, 0), lane), bfrag16(U[0]));
-                    if (b >= 2) z = mma(z, frag_dt(Ad, dt_index(b, 0), lane), bfrag_hi(U[0], U[1]));
-                    if (b == 3) z = mma(z, frag_dt(Ad, dt_index(3, 1), lane), bfrag_hi(U[2], zero));
+                    if (b >= 2) z = mma(z, frag_dt(Ad, dt_index(b, 0), lane), bfrag(U[0], U[1]));
+                    if (b == 3) z = mma(z, frag_dt(Ad, dt_index(3, 1), lane), bfrag(U[2], zero));
                     U[b] = mma16(z, frag_t16(Tt, b, lane), bfrag16(z));
                 }
             } else {
@@ -740,14 +739,13 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             // O^T = (S^T Q^T) diag(scale e) + U^T P^T; lane: token 16 tt + l%16, d_v
             // columns col0 + 4 (l/16) + i
             if constexpr (WITH_O) {
-                Frag uh[KBT], ul[KBT];
+                Frag uh[KBT];
 #pragma unroll
                 for (int kb = 0; kb < KBT; ++kb) {
-                    if constexpr (P::kBF16) bfrag_split(U[2 * kb], U[2 * kb + 1], uh[kb], ul[kb]);
+                    if constexpr (P::kBF16) uh[kb] = bfrag(U[2 * kb], U[2 * kb + 1]);
                     else uh[kb] = U[kb];
                 }
                 const char *Ph = buf + L::oPh;
-                const char *Pl = buf + L::oPl;
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
                     OT[tt] *= gEs[16 * tt + lr];
@@ -755,10 +753,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                     for (int kb = 0; kb < KBT; ++kb) {
                         if (kb * P::KB < 16 * tt + 16) {
                             if constexpr (P::kBF16) {
-                                const Frag ph = frag_dt(Ph, dt_index(tt, kb), lane);
-                                OT[tt] = mma(OT[tt], uh[kb], ph);
-                                OT[tt] = mma(OT[tt], ul[kb], ph);
-                                OT[tt] = mma(OT[tt], uh[kb], frag_dt(Pl, dt_index(tt, kb), lane));
+                                OT[tt] = mma(OT[tt], uh[kb], frag_dt(Ph, dt_index(tt, kb), lane));
                             } else {
                                 OT[tt] = mma(OT[tt], uh[kb],
                                              frag_tile(reinterpret_cast<const float *>(Ph), tri_index(tt, kb), lane));
@@ -800,7 +795,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt) S[rt] *= rn;
                 }
-                Frag dh[KBT], dl[KBT];
+                Frag dh[KBT];
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
                     const f32x4 l4 = *reinterpret_cast<const f32x4 *>(gL + 16 * tt + 4 * lg);
@@ -809,7 +804,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                 }
 #pragma unroll
                 for (int kb = 0; kb < KBT; ++kb) {
-                    if constexpr (P::kBF16) bfrag_split(U[2 * kb], U[2 * kb + 1], dh[kb], dl[kb]);
+                    if constexpr (P::kBF16) dh[kb] = bfrag(U[2 * kb], U[2 * kb + 1]);
                     else dh[kb] = U[kb];
                 }
 #pragma unroll
@@ -818,9 +813,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
 #pragma unroll
                     for (int kb = 0; kb < KBT; ++kb) {
                         if constexpr (P::kBF16) {
-                            const Frag kf = frag_kt<RBK>(Ks, rt, kb, lane);
-                            s = mma(s, kf, dh[kb]);
-                            s = mma(s, kf, dl[kb]);
+                            s = mma(s, frag_kt<RBK>(Ks, rt, kb, lane), dh[kb]);
                         } else {
                             s = mma(s, frag_cols_f32<RBK>(Ks, 16 * rt, kb, lane), dh[kb]);
                         }
@@ -831,15 +824,18 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             sync_lds();   // this chunk's buffer is free; the next one is prepared
         }
 
-        // ---- state write-back: S = sig S~, sig from the last chunk's gate rows
+        // ---- state write-back: S = sig S~, sig from the last chunk's gate rows (lane
+        // indices derived afresh, so that no address stays live across the chunk loop)
         const float sig = nch > 0 ? reinterpret_cast<const float *>(smem + ((nch - 1) & 1) * L::BUF +
                                                                     L::oGate)[6 * CH + 1]
                                   : 1.f;
+        int wl = lane0;
+        asm volatile("" : "+v"(wl));
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                a.S_out[sbase + (int64_t)(16 * rt + 4 * lg + i) * DV + col0 + lr] = S[rt][i] * sig;
+                a.S_out[sbase + (int64_t)(16 * rt + 4 * (wl >> 4) + i) * DV + col0 + (wl & 15)] = S[rt][i] * sig;
     } else {
         // =====================================================================
         // prep waves: chunk c + 1's operands while the state waves process chunk c
@@ -925,13 +921,16 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                     if constexpr (P::kBF16) {
                         const bool sw = s_sw;
                         const int oa = s_oa[j], ob = s_ob[j];
+                        // bf16 in global memory, fp16 in LDS (the matrix operand type)
                         const u32x4 a0 = kpf[2 * j], a1 = kpf[2 * j + 1];
-                        const u32x4 k0 = {a0.x, a0.y, a1.x, a1.y}, k1 = {a0.z, a0.w, a1.z, a1.w};
+                        const u32x4 k0 = {bf2_to_h2(a0.x), bf2_to_h2(a0.y), bf2_to_h2(a1.x), bf2_to_h2(a1.y)};
+                        const u32x4 k1 = {bf2_to_h2(a0.z), bf2_to_h2(a0.w), bf2_to_h2(a1.z), bf2_to_h2(a1.w)};
                         *reinterpret_cast<u32x4 *>(Ks + oa) = sw ? k1 : k0;
                         *reinterpret_cast<u32x4 *>(Ks + ob) = sw ? k0 : k1;
                         if (WITH_O) {
                             const u32x4 b0 = qpf[2 * j], b1 = qpf[2 * j + 1];
-                            const u32x4 q0 = {b0.x, b0.y, b1.x, b1.y}, q1 = {b0.z, b0.w, b1.z, b1.w};
+                            const u32x4 q0 = {bf2_to_h2(b0.x), bf2_to_h2(b0.y), bf2_to_h2(b1.x), bf2_to_h2(b1.y)};
+                            const u32x4 q1 = {bf2_to_h2(b0.z), bf2_to_h2(b0.w), bf2_to_h2(b1.z), bf2_to_h2(b1.w)};
                             *reinterpret_cast<u32x4 *>(Qs + oa) = sw ? q1 : q0;
                             *reinterpret_cast<u32x4 *>(Qs + ob) = sw ? q0 : q1;
                         }
@@ -944,11 +943,13 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             }
             if (pw == GW) {
                 // the state waves keep S~ = S / sig: the chunk's decay e_last goes into sig,
-                // and into S~ (factor rn) only when sig would drop below 2^-60 or the chunk
-                // holds a reset (e_last = 0); then sig restarts at 1
+                // and into S~ (factor rn) only when sig would drop below kSigMin or the
+                // chunk holds a reset (e_last = 0); then sig restarts at 1.  fp16 operands
+                // (the bf16 path) keep |S~| <= 64 |S| that way; fp32 ones only need range.
+                constexpr float kSigMin = P::kBF16 ? 0x1p-6f : 0x1p-60f;
                 const float el = __shfl(gt.e, 63);
                 const float cand = el * sig;
-                const bool renorm = !(cand >= 0x1p-60f);
+                const bool renorm = !(cand >= kSigMin);
                 const float rn = renorm ? cand : 1.f;
                 const float sig_new = renorm ? 1.f : cand;
                 float *gH = reinterpret_cast<float *>(buf + L::oGate);

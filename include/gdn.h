@@ -42,6 +42,17 @@
  * word (read it with gdn_device_status), skips the offending sequences and leaves
  * their outputs unspecified.  Non-finite q/k/v/beta or g > 0 are not checked; the
  * result is then undefined and gdn_state_relerr's non-finite count exposes it.
+ *
+ * Arithmetic: the state is fp32 throughout.  fp32 inputs use fp32 matrix products.
+ * bf16 inputs use matrix products with fp16 operands and fp32 accumulation: q and k
+ * enter exactly (bf16 values of magnitude in [2^-14, 65504], which L2-normalised q and
+ * k are; smaller entries round to fp16 subnormals), the intermediate state and pseudo-
+ * values are rounded to fp16 once per product (relative error <= 2^-11).  Their range
+ * is checked nowhere: state entries, and v-sized intermediates, must stay below ~10^3
+ * in magnitude (the state is scaled by at most 64 internally); beyond that the fp16
+ * operands overflow and the outputs turn non-finite (again exposed by the non-finite
+ * count).  Gated DeltaNet states with unit keys, beta in [0, 1] and O(1) values stay
+ * orders of magnitude inside this.
  */
 #ifndef GDN_H
 #define GDN_H

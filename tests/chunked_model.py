@@ -37,6 +37,11 @@ def split(x):
     return hi, bf16(np.asarray(x, np.float64) - hi)
 
 
+def f16(x):
+    """Round to IEEE binary16 (round to nearest even), returned as float64."""
+    return np.asarray(x, np.float64).astype(np.float16).astype(np.float64)
+
+
 def gates(g):
     """Reset-aware in-chunk gate scan. Returns H, e, Gam (lower incl. diagonal)."""
     n = len(g)
@@ -59,13 +64,16 @@ def gates(g):
 
 
 class Policy:
-    """Which operands are rounded to bf16 (hi) or split into hi + lo bf16 pairs."""
+    """Which operands are rounded to bf16 (hi), split into hi + lo bf16 pairs (split) or
+    rounded to fp16 (f16); ``qk`` rounds q and k themselves ("f16": the matrix operands are
+    fp16 copies of the bf16 inputs), ``p_diag`` puts P's diagonal into the rounded P."""
 
     def __init__(self, exact=True, S_in_X="hi", S_in_O="split", Y_in_U="hi", T="hi",
-                 P="hi", U_in_O="split", U_in_S="split", o_round=True):
+                 P="hi", U_in_O="split", U_in_S="split", o_round=True, qk="exact", p_diag=False):
         self.exact = exact
         self.S_in_X, self.S_in_O, self.Y_in_U, self.T = S_in_X, S_in_O, Y_in_U, T
         self.P, self.U_in_O, self.U_in_S, self.o_round = P, U_in_O, U_in_S, o_round
+        self.qk, self.p_diag = qk, p_diag
 
     @staticmethod
     def apply(x, mode):
@@ -75,10 +83,16 @@ class Policy:
             return [bf16(x)]
         if mode == "split":
             return list(split(x))
+        if mode == "f16":
+            return [f16(x)]
         raise ValueError(mode)
 
 
 EXACT = Policy(exact=True)
+# the bf16-input path of the kernel: every matrix operand an fp16 rounding of its fp32 value
+# (q, k exactly, being bf16 values within the fp16 range); o rounded to bf16 on output
+F16_OPERANDS = Policy(exact=False, S_in_X="f16", S_in_O="f16", Y_in_U="f16", T="f16", P="f16",
+                      U_in_O="f16", U_in_S="f16", qk="f16", p_diag=True)
 
 
 def _prod(Aparts, Bparts, max_terms=3):
@@ -114,15 +128,20 @@ def chunk_chain(q, k, v, g, beta, S0=None, C=64, scale=1.0, pol: Policy = EXACT)
             Ob = e[:, None] * (Q @ S) + Pd[:, None] * U + P @ U
             S = e[-1] * S + K.T @ (Gam[-1][:, None] * U)
         else:
-            X = _prod([K], Policy.apply(S, pol.S_in_X))
+            Kr, Qr = (f16(K), f16(Q)) if pol.qk == "f16" else (K, Q)
+            X = _prod([Kr], Policy.apply(S, pol.S_in_X))
             Y = b[:, None] * (V - e[:, None] * X)
             Toff = Tm - np.eye(n)
             U = Y + _prod(Policy.apply(Toff, pol.T), Policy.apply(Y, pol.Y_in_U))
-            QS = _prod([Q], Policy.apply(S, pol.S_in_O))
-            Ob = e[:, None] * QS + Pd[:, None] * U + _prod(Policy.apply(P, pol.P),
-                                                           Policy.apply(U, pol.U_in_O))
+            QS = _prod([Qr], Policy.apply(S, pol.S_in_O))
+            if pol.p_diag:
+                Ob = e[:, None] * QS + _prod(Policy.apply(P + np.diag(Pd), pol.P),
+                                             Policy.apply(U, pol.U_in_O))
+            else:
+                Ob = e[:, None] * QS + Pd[:, None] * U + _prod(Policy.apply(P, pol.P),
+                                                               Policy.apply(U, pol.U_in_O))
             Ud = Gam[-1][:, None] * U
-            S = e[-1] * S + _prod([K.T], Policy.apply(Ud, pol.U_in_S))
+            S = e[-1] * S + _prod([Kr.T], Policy.apply(Ud, pol.U_in_S))
         O[t0:t0 + n] = scale * Ob
     if not ex and pol.o_round:
         O = bf16(O)

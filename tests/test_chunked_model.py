@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from chunked_model import Policy, bf16, chunk_chain, gates, split
+from chunked_model import F16_OPERANDS, Policy, bf16, chunk_chain, f16, gates, split
 
 
 def _case(rs, T, dk, dv, g_mu=-4.0, g_sigma=1.0):
@@ -72,22 +72,28 @@ def test_bf16_rounding_helper():
     assert r[0] == 1.0 and r[1] == 1.0 and r[2] == 1.0 + 4 * 2 ** -8 and r[3] == -2.5
     hi, lo = split(np.pi)
     assert abs(hi + lo - np.pi) < 2 ** -16 * np.pi
+    # binary16: 11 significant bits, ties to even, 2^-24 the smallest subnormal
+    h = f16(np.array([1.0 + 2 ** -11, 1.0 + 3 * 2 ** -11, 65504.0, 2 ** -24, -0.1]))
+    assert h[0] == 1.0 and h[1] == 1.0 + 2 ** -9 and h[2] == 65504.0 and h[3] == 2 ** -24
+    assert abs(h[4] + 0.1) <= 2 ** -15
 
 
 @pytest.mark.slow
-def test_precision_layout_meets_bf16_tolerance():
-    """The bf16 operand layout the kernel uses stays within 3e-3 on S and on o.
+@pytest.mark.parametrize("g_mu,g_sigma", [(-5.0, 1.0), (-8.0, 0.5), (-2.0, 1.0)])
+def test_precision_layout_meets_bf16_tolerance(g_mu, g_sigma):
+    """The fp16-operand layout of the bf16 path stays well within 3e-3 on S and on o.
 
-    Reduced size (d = 128, T = 1024, config-1 gates); the full-size check runs on the
-    GPU against the oracle.
+    Reduced size (d = 128, T = 1024; the stack's, the slow-decay and a fast-decay gate
+    distribution); the full-size checks run on the GPU against the oracle.  The margin
+    asked for here (S < 1e-3, o < 2.2e-3 with bf16-rounded o, whose own rounding floor is
+    ~1.7e-3) leaves the GPU's summation order room.
     """
     rs = np.random.default_rng(21)
     T, d = 1024, 128
-    q, k, v, g, beta = _case(rs, T, d, d, g_mu=-5.0)
+    q, k, v, g, beta = _case(rs, T, d, d, g_mu=g_mu, g_sigma=g_sigma)
     q, k, v = bf16(q), bf16(k), bf16(v)
     S, o = _oracle_chain(q, k, v, g, beta)
-    pol = Policy(exact=False)
-    Sc, oc = chunk_chain(q, k, v, g, beta, pol=pol)
+    Sc, oc = chunk_chain(q, k, v, g, beta, pol=F16_OPERANDS)
     eS = np.linalg.norm(Sc - S) / np.linalg.norm(S)
     eo = np.linalg.norm(oc - o) / np.linalg.norm(o)
-    assert eS < 3e-3 and eo < 3e-3, (eS, eo)
+    assert eS < 1e-3 and eo < 2.2e-3, (eS, eo)
