@@ -237,3 +237,21 @@ def test_fast_decay_renormalises_the_stored_state(mu, dtype):
     for mode in ("replay", "prefill"):
         inp, S, o, cu_out, eS, eo = _case(w, mode)
         assert eS <= tol and eo <= tol, (mode, eS, eo)
+
+
+@pytest.mark.parametrize("mu", [-5.0, -8.0])
+def test_bf16_large_values_inside_the_fp16_operand_range(mu):
+    # v scaled by 128 (exact in bf16): state entries of a few hundred, so the stored state
+    # S / sig (up to 64 |S| between renormalisations) approaches the fp16 operand range the
+    # header states; the error must stay that of unit-scale values
+    w = W.small(W.config(1), L=[1500, 700], r=[1200, 300], h_qk=2, h_v=4, g_mu=mu, g_sigma=0.5)
+    inp = W.make_inputs(w)
+    inp["v"] = (inp["v"].float() * 128.0).to(inp["v"].dtype)
+    for mode in ("replay", "prefill"):
+        S, o, _ = gpu_run(to_dev(inp), mode)
+        torch.cuda.synchronize()
+        S_ref, o_ref = oracle_run(inp, mode)
+        eS, eo = compare(inp, mode, S, o, S_ref, o_ref)
+        say("  mu %.0f %s: max|S| %.1f  relerr S %.3e  o %.3e" % (mu, mode, float(np.abs(S_ref).max()), eS, eo))
+        assert np.isfinite(eS) and np.isfinite(eo)
+        assert eS <= TOL["bf16"] and eo <= TOL["bf16"], (mode, eS, eo)
