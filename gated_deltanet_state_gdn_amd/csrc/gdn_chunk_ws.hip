@@ -913,9 +913,11 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             int lane = lane0;
             asm volatile("" : "+v"(lane));
             // step 1 is what every prep wave's barrier, and through it the state waves,
-            // waits for: it issues ahead of the state waves' work on the same SIMD (measured:
-            // 6 % off the 36-layer replay; raising the Gram tiles as well gains less)
-            __builtin_amdgcn_s_setprio(3);
+            // waits for: with all eight state waves busy it issues ahead of their work on the
+            // same SIMD (measured: 6 % off the 36-layer replay; raising the Gram tiles as well
+            // gains less); a column-slice block, with one or a few state waves, gains nothing
+            // from it and loses up to 7 %, so it keeps the default priority
+            if (nact == NSW) __builtin_amdgcn_s_setprio(3);
             char *buf = smem + (cc & 1) * L::BUF;
             char *Ks = buf + L::oK;
             char *Qs = buf + L::oQ;
