@@ -67,7 +67,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus %d is not supported "
+        print(json.dumps({"error": "the replay benchmark runs on one GPU; --gpus %d is not supported "
                                    "(the path shards by (sequence, v-head) with no exchange, "
                                    "see the design notes)" % args.gpus}))
         sys.exit(2)

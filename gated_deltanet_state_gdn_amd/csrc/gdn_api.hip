@@ -126,7 +126,7 @@ const char *gdn_status_str(int32_t s)
     case GDN_ERR_NULL: return "required pointer is NULL";
     case GDN_ERR_SHAPE: return "invalid or inconsistent sizes";
     case GDN_ERR_DTYPE: return "unknown or unsupported dtype combination";
-    case GDN_ERR_UNSUPPORTED: return "head dims / dtype not supported by this build";
+    case GDN_ERR_UNSUPPORTED: return "head dims / dtype combination not supported by the library";
     case GDN_ERR_ALIGN: return "pointer not 16-byte aligned";
     case GDN_ERR_WORKSPACE: return "workspace missing or too small";
     case GDN_ERR_LAUNCH: return "kernel launch failed";
