@@ -201,31 +201,36 @@ __device__ __forceinline__ f32x4 frag_cols_f32(const char *M, int c0, int kb, in
     return f;
 }
 
-// bf16 tile pairs: the 16 x 32 block (16-row block ti, 32-column block kb) of a 64x64
-// lower-triangular matrix, rows of 64 bytes; logical chunk g of row r holds columns
-// 4g..4g+3 of tile (ti, 2kb) then of tile (ti, 2kb+1), stored at chunk g ^ ((r >> 2) & 3).
+// The small operand tiles are stored in fragment order: the lane that reads a fragment
+// finds it at 16 (or 8) bytes times its lane index, and the lane that writes it uses the
+// same index, since producer and consumer share the A-operand layout (lane l: row l%16,
+// columns 4 (l/16) .. +3 of a 16x16 tile).  Consecutive lanes then touch consecutive
+// bytes, which the LDS serves without bank conflicts (a row-major layout with 32- or
+// 64-byte rows measured 2.3e7 and 1.7e7 conflict cycles per 36-layer launch).
+//
+// bf16-path tile pairs: the 16 x 32 block (16-row block ti, 32-column block kb) of a
+// 64x64 lower-triangular matrix as one 16-byte fragment per lane: columns 4 (l/16) .. +3
+// of tile (ti, 2kb), then of tile (ti, 2kb+1), of row l%16.
 // Pair index of (ti, kb), kb <= ti/2:  0:(0,0) 1:(1,0) 2:(2,0) 3:(2,1) 4:(3,0) 5:(3,1).
 __device__ __forceinline__ int dt_index(int ti, int kb) { return ti < 2 ? ti : 2 * ti - 2 + kb; }
-__device__ __forceinline__ int dt_at(int r, int g) { return r * 64 + 16 * (g ^ ((r >> 2) & 3)); }
 __device__ __forceinline__ h16x8 frag_dt(const char *T, int pair, int lane) {
-    return __builtin_bit_cast(
-        h16x8, *reinterpret_cast<const u32x4 *>(T + pair * 1024 + dt_at(lane & 15, lane >> 4)));
+    return __builtin_bit_cast(h16x8, *reinterpret_cast<const u32x4 *>(T + pair * 1024 + 16 * lane));
 }
 
-// 16x16 tiles, row-major (32-byte rows in bf16, 64-byte rows in fp32): T_bb - I, and for
-// fp32 inputs also -A and P; lower tile (ti, tj) of a 64x64 matrix at ti*(ti+1)/2 + tj.
+// 16x16 tiles (T_bb - I; for fp32 inputs also -A and P), one 4-element fragment per lane;
+// lower tile (ti, tj) of a 64x64 matrix at ti*(ti+1)/2 + tj.
 __device__ __forceinline__ int tri_index(int ti, int tj) { return ti * (ti + 1) / 2 + tj; }
 // Operands of a 16x16x16 product (4 contraction indices per lane), for the products
 // whose other half would be zero: the first tile of a tile pair and a 16x16 tile, both
 // in the A-operand layout (lane l: row l%16, columns 4 (l/16) .. +3).
 __device__ __forceinline__ u32x2 frag_dt_first(const char *T, int pair, int lane) {
-    return *reinterpret_cast<const u32x2 *>(T + pair * 1024 + dt_at(lane & 15, lane >> 4));
+    return *reinterpret_cast<const u32x2 *>(T + pair * 1024 + 16 * lane);
 }
 __device__ __forceinline__ u32x2 frag_t16(const uint16_t *T, int tile, int lane) {
-    return *reinterpret_cast<const u32x2 *>(T + tile * 256 + (lane & 15) * 16 + 4 * (lane >> 4));
+    return *reinterpret_cast<const u32x2 *>(T + tile * 256 + 4 * lane);
 }
 __device__ __forceinline__ f32x4 frag_tile(const float *T, int tile, int lane) {
-    return *reinterpret_cast<const f32x4 *>(T + tile * 256 + (lane & 15) * 16 + 4 * (lane >> 4));
+    return *reinterpret_cast<const f32x4 *>(T + tile * 256 + 4 * lane);
 }
 
 // ---------------------------------------------------------------- register operands
@@ -393,12 +398,12 @@ __device__ __forceinline__ f32x4 tile_store(char *buf, float hr, float br, int r
         pv[e] = scale * gam * qk[e];
     }
     if constexpr (P::kBF16) {
-        const int eo = dt_index(ti, tj >> 1) * 1024 + dt_at(lr, lg) + 8 * (tj & 1);
+        const int eo = dt_index(ti, tj >> 1) * 1024 + 16 * lane + 8 * (tj & 1);
         *reinterpret_cast<u32x2 *>(buf + L::oA + eo) = u32x2{pk_h(av[0], av[1]), pk_h(av[2], av[3])};
         if constexpr (WITH_O)
             *reinterpret_cast<u32x2 *>(buf + L::oPh + eo) = u32x2{pk_h(pv[0], pv[1]), pk_h(pv[2], pv[3])};
     } else {
-        const int eo = tri_index(ti, tj) * 256 + lr * 16 + 4 * lg;
+        const int eo = tri_index(ti, tj) * 256 + 4 * lane;
         *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(buf + L::oA) + eo) = av;
         if constexpr (WITH_O) *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(buf + L::oPh) + eo) = pv;
     }
@@ -448,7 +453,7 @@ __device__ __forceinline__ void diag_inverse(f32x4 Nr, E *Tt, int lane) {
     const f32x4 P2r = mm16<BF>(P1r, N4c, P1r);        // P1 (I + N^4)
     const f32x4 Tr = mm16<BF>(P2r, N8c, P2r);         // P2 (I + N^8)
     const f32x4 Tm = Tr - I4;
-    E *row = Tt + lr * 16 + 4 * lg;
+    E *row = Tt + 4 * lane;
     if constexpr (sizeof(E) == 2) {
         *reinterpret_cast<u32x2 *>(row) = u32x2{pk_h(Tm[0], Tm[1]), pk_h(Tm[2], Tm[3])};
     } else {
