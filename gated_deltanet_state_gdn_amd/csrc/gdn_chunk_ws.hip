@@ -16,7 +16,7 @@
 //     U_b = Z_b + (T_bb - I) Z_b,   Z_b = Y_b - sum_{j<b} A_bj U_j,   T_bb = (I + A_bb)^{-1}.
 //
 // Work decomposition: one workgroup per (sequence, v-head, d_v block), split into two
-// roles that run concurrently on double-buffered LDS:
+// roles that run concurrently on two LDS chunk buffers:
 //   * state waves (one per 16-column tile of S): the sequential pass over the chunks.
 //     S never leaves their MFMA accumulators; the columns of S evolve independently
 //     because (I - b k k^T) acts on the d_k side only, so they exchange nothing.
@@ -433,9 +433,9 @@ __device__ __forceinline__ f32x4 mm16(f32x4 c, f32x4 x, f32x4 y) {
 // T_bb - I for one 16x16 block from N = -A_bb (strictly lower, so N^16 = 0) in the
 // A-operand layout, as the product
 //     T = (I + A)^{-1} = (I - N)^{-1} = I + N + ... + N^15 = (I + N)(I + N^2)(I + N^4)(I + N^8),
-// every factor formed in registers on the matrix cores (bf16 operands for bf16 inputs:
-// T - I is stored in bf16 for the solve anyway); stored in the A-operand layout (lane l:
-// row l%16, columns 4 (l/16) .. +3).
+// every factor formed in registers on the matrix cores (fp16 operands for bf16 inputs:
+// T - I is stored in fp16 for the solve anyway); stored in fragment order (lane l: row
+// l%16, columns 4 (l/16) .. +3, at 4 l).
 template <class E>
 __device__ __forceinline__ void diag_inverse(f32x4 Nr, E *Tt, int lane) {
     constexpr bool BF = sizeof(E) == 2;
