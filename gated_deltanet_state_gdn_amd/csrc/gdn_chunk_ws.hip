@@ -187,6 +187,18 @@ __device__ __forceinline__ h16x8 frag_kt(const char *K, int rt, int kb, int lane
     const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
     return __builtin_bit_cast(h16x8, u32x4{ua.x, ua.y, ub.x, ub.y});
 }
+// V values of one 16-row tile in the accumulator layout, from the bf16 V rows staged in the
+// same permuted, swizzled layout as K: lane l gets V[16 tt + 4 (l/16) + i][16 ct + l%16],
+// i = 0..3, as bf16 pairs (element i in half i%2 of word i/2).  One transposing read: lane
+// m = 4 y + x of group g points at row 16 tt + 4 g + y, columns 16 ct + 4 x .. +3.
+template <int RB>
+__device__ __forceinline__ u32x2 frag_v(const char *V, int ct, int tt, int lane) {
+    const int m = lane & 15;
+    const int row = 16 * tt + 4 * (lane >> 4) + (m >> 2);
+    const char *p = V + chunk_at<RB>(row, 4 * (ct >> 1) + (m & 3)) + 8 * (ct & 1);
+    typedef __attribute__((address_space(3))) i16x4 *lds_i16x4;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)p));
+}
 // fp32 fragment of M^T (the rows of M are the contraction index): lane l gives column
 // c0 + l%16 and rows 16 kb + 4 (l/16) + i.
 template <int RB>
@@ -278,10 +290,11 @@ __device__ __forceinline__ void prep_sync(int *ctr, int &target, int lane, int *
 // ---------------------------------------------------------------- LDS plan
 // Two chunk buffers (the state waves read one while the prep waves fill the other),
 // then a few words.
-template <int DK, class P, bool WITH_O>
+template <int DK, int W, class P, bool WITH_O>
 struct Lds {
     typedef typename P::E E;
     static constexpr int RBK = DK * (int)sizeof(E);          // K / Q row bytes
+    static constexpr int RBV = W * 2;                          // V row bytes (bf16 inputs)
     static constexpr int TILE = 256 * (int)sizeof(E);          // one 16x16 tile
     static constexpr int NTA = P::kBF16 ? 6 : 10;              // tile pairs (bf16) / tiles (fp32)
     static constexpr int UNIT = P::kBF16 ? 1024 : TILE;
@@ -291,7 +304,9 @@ struct Lds {
     static constexpr int oGate = 0;
     static constexpr int oK = 8 * CH * 4;
     static constexpr int oQ = oK + CH * RBK;
-    static constexpr int oA = oQ + (WITH_O ? CH * RBK : 0);     // -A
+    // V of the block's column range (bf16 inputs; fp32 inputs read V from global memory)
+    static constexpr int oV = oQ + (WITH_O ? CH * RBK : 0);
+    static constexpr int oA = oV + (P::kBF16 ? CH * RBV : 0);  // -A
     static constexpr int oT = oA + NTA * UNIT;                   // 4 tiles T_bb - I
     static constexpr int oPh = oT + 4 * TILE;                    // P
     static constexpr int BUF = oPh + (WITH_O ? NTA * UNIT : 0);
@@ -508,7 +523,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
     constexpr int NTHR = 64 * (NSW + NPW);
     typedef typename P::E E;
     typedef typename P::Frag Frag;
-    typedef Lds<DK, P, WITH_O> L;
+    typedef Lds<DK, W, P, WITH_O> L;
     constexpr int RT = DK / 16;            // row tiles of S
     constexpr int KBK = DK / P::KB;        // k-blocks over d_k
     constexpr int KBT = CH / P::KB;        // k-blocks over the chunk's tokens
@@ -636,8 +651,10 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                 S[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
-        // V rows of a chunk in accumulator layout (rows past the window read as 0; a
-        // chunk past the window gets an empty buffer and touches no memory)
+        // fp32 inputs: V rows of a chunk in accumulator layout, from global memory (rows
+        // past the window read as 0; a chunk past the window gets an empty buffer and
+        // touches no memory).  bf16 inputs take V from the chunk buffer instead.
+        const int vct = (c_lo - cb * W) / 16 + wave;   // 16-column tile of the staged V rows
         const uint32_t vrow = (uint32_t)a.h_v * (uint32_t)(DV * sizeof(E));   // bytes per token
         typename Raw<P>::T vreg[4][4];
         auto fetch_v = [&](int64_t cc) {
@@ -660,7 +677,9 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         // the initial state is in registers before the loop, so no wait for it is left
         // inside the loop (vmcnt(0) only; expcnt and lgkmcnt at their maxima)
         __builtin_amdgcn_s_waitcnt(0x0F70);
-        if (nch > 0) fetch_v(0);
+        if constexpr (!P::kBF16) {
+            if (nch > 0) fetch_v(0);
+        }
         sync_lds();                                  // chunk 0 prepared
 
         for (int64_t c = 0; c < nch; ++c) {
@@ -703,10 +722,20 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             for (int tt = 0; tt < 4; ++tt) {
                 const f32x4 br = *reinterpret_cast<const f32x4 *>(gB + 16 * tt + 4 * lg);
                 const f32x4 er = *reinterpret_cast<const f32x4 *>(gE + 16 * tt + 4 * lg);
+                f32x4 vv;
+                if constexpr (P::kBF16) {
+                    const u32x2 w = frag_v<L::RBV>(buf + L::oV, vct, tt, lane);
+                    vv = f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                                __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+                } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) X[tt][i] = br[i] * (v_at<P>(vreg[tt][i]) - er[i] * X[tt][i]);
+                    for (int i = 0; i < 4; ++i) vv[i] = v_at<P>(vreg[tt][i]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) X[tt][i] = br[i] * (vv[i] - er[i] * X[tt][i]);
             }
-            fetch_v(c0 + CH);   // lands while this chunk is processed (past the end: no access)
+            // fp32 inputs: the next chunk's V lands while this one is processed
+            if constexpr (!P::kBF16) fetch_v(c0 + CH);
 
             // (I + A) U = Y by 16-row block forward substitution
             f32x4 U[4];
@@ -871,6 +900,26 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         const int spt = 64 * pw + lane0;
         const bool s_act = UT >= TH || spt < UT;   // with fewer units than threads, the last waves idle
         const int spu = spt % NPU, srow = spt / NPU;
+        // V rows (bf16 inputs): the same kind of units over the block's columns, rounded out
+        // to whole 32-column blocks, at their places in a W-column row; copied without
+        // conversion (the state waves read them with transposing reads).  At most one unit
+        // per thread.
+        static_assert(CH * (W / 16) <= TH, "V unit map");
+        constexpr bool STAGE_V = P::kBF16;
+        const uint32_t vrowp = (uint32_t)a.h_v * (uint32_t)(DV * sizeof(E));   // bytes per token
+        u32x4 vpf[2];
+        const int nuv = (ncols < 32 ? 32 : ncols) / 16;          // units per row
+        const int srowv = spt >> __builtin_ctz(nuv);
+        const int spuv = 2 * ((c_lo - cb * W) >> 5) + (spt & (nuv - 1));
+        const bool v_act = STAGE_V && srowv < CH;
+        const uint32_t v_vo = (uint32_t)srowv * vrowp + (uint32_t)(64 * (spuv >> 1) + 16 * (spuv & 1));
+        const bool v_sw = (spuv & 4) != 0;
+        int v_oa = 0, v_ob = 0;
+        if constexpr (STAGE_V) {
+            const int c0 = 4 * (spuv >> 1) + 2 * (spuv & 1);
+            v_oa = chunk_at<L::RBV>(srowv, v_sw ? c0 + 1 : c0);
+            v_ob = chunk_at<L::RBV>(srowv, v_sw ? c0 : c0 + 1);
+        }
         const uint32_t s_vo = (uint32_t)srow * krow +
                               (uint32_t)(P::kBF16 ? 64 * (spu >> 1) + 16 * (spu & 1) : 16 * spu);
         const bool s_sw = P::kBF16 && (spu & 4) != 0;
@@ -907,11 +956,18 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                         if (WITH_O) qpf[VPU * j + v] = __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0);
                     }
             }
+            if constexpr (STAGE_V) {
+                if (v_act) {
+                    const Rsrc rv = make_rsrc(vg + ((t0 * a.h_v + h) * (int64_t)DV + cb * W), ln * (int64_t)vrowp);
+                    vpf[0] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_vo, 0, 0);
+                    vpf[1] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_vo + 32u, 0, 0);
+                }
+            }
         };
 
         // prepare chunk cc into buffer cc & 1:
-        //   step 1: K, Q (fetched one chunk earlier) and the gates (scanned one chunk
-        //           earlier) into LDS; fetch chunk cc + 1
+        //   step 1: K, Q, V (bf16 inputs; fetched one chunk earlier) and the gates
+        //           (scanned one chunk earlier) into LDS; fetch chunk cc + 1
         //   step 2: after the prep waves' barrier, each wave's Gram tiles and diagonal
         //           inverse; the gate scan of chunk cc + 1 (wave GW)
         auto prep = [&](int64_t cc) {
@@ -950,6 +1006,15 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                         *reinterpret_cast<u32x4 *>(Ks + o) = kpf[j];
                         if (WITH_O) *reinterpret_cast<u32x4 *>(Qs + o) = qpf[j];
                     }
+                }
+            }
+            if constexpr (STAGE_V) {
+                if (v_act) {
+                    char *Vs = buf + L::oV;
+                    const u32x4 a0 = vpf[0], a1 = vpf[1];
+                    const u32x4 v0 = {a0.x, a0.y, a1.x, a1.y}, v1 = {a0.z, a0.w, a1.z, a1.w};
+                    *reinterpret_cast<u32x4 *>(Vs + v_oa) = v_sw ? v1 : v0;
+                    *reinterpret_cast<u32x4 *>(Vs + v_ob) = v_sw ? v0 : v1;
                 }
             }
             if (pw == GW) {
