@@ -23,8 +23,8 @@
 //     The outputs are formed transposed (O^T = S^T Q^T + U^T P^T), which puts four
 //     consecutive d_v entries of one token in a lane: one vector store per 16 tokens.
 //   * eight prep waves: everything that does not depend on S, one chunk ahead -- the
-//     chunk's K and Q in LDS (all eight), the Gram products forming -A and P and the
-//     diagonal-block inverses (seven), the gate scan (one).
+//     chunk's K and Q (and, for bf16 inputs, V) in LDS (all eight), the Gram products
+//     forming -A and P and the diagonal-block inverses (seven), the gate scan (one).
 // The state waves keep S / sig instead of S, sig being the product of the chunk decays
 // since the last renormalisation, so the per-chunk decay e_last costs no pass over S.
 // One workgroup barrier per chunk hands a prepared buffer to the state waves; the
