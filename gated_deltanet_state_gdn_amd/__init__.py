@@ -69,7 +69,8 @@ def gdn_workspace_bytes(desc: GdnDesc) -> int:
 
 
 def workspace(desc: GdnDesc, device) -> torch.Tensor:
-    return torch.empty(gdn_workspace_bytes(desc), dtype=torch.uint8, device=device)
+    """A zero-filled workspace (its status word accumulates bits until read)."""
+    return torch.zeros(gdn_workspace_bytes(desc), dtype=torch.uint8, device=device)
 
 
 def _check(code: int, where: str):

@@ -9,8 +9,9 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
 GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 GDN_ERR_ALIGN, GDN_ERR_WORKSPACE, GDN_ERR_LAUNCH, GDN_ERR_DEVICE_INPUT, GDN_ERR_HIP = 5, 6, 7, 8, 9
+GDN_ERR_DEVICE_WAIT = 10
 GDN_F32, GDN_BF16 = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 # every symbol include/gdn.h declares
 EXPORTS = ("gdn_abi_version", "gdn_status_str", "gdn_replay_len", "gdn_workspace_bytes",

@@ -20,7 +20,7 @@
 // Pass 1: one wavefront per (sequence, v-head) walks the sequence backwards, 512
 // tokens per step (8 per lane, in flight together), with a wavefront prefix sum,
 // and stops at the first crossing.  Pass 2: one workgroup takes the maximum over
-// heads, clamps it, validates cu_seqlens and writes the status word.
+// heads, clamps it, validates cu_seqlens and sets the status word's bad-input bit.
 #include "gdn_common.h"
 
 namespace gdn {
@@ -128,7 +128,7 @@ __global__ void __launch_bounds__(256) adaptive_reduce_kernel(const int32_t *cu,
         r_out[n] = (int32_t)m;
     }
     bad = __syncthreads_or(bad);
-    if (threadIdx.x == 0) *status = bad ? kStatusBadInput : kStatusOk;
+    if (threadIdx.x == 0 && bad) atomicOr(status, kStatusBitInput);
 }
 
 }  // namespace

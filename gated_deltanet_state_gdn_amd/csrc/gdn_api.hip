@@ -56,8 +56,8 @@ int32_t check_desc(const gdn_desc *d, bool replay)
         return GDN_ERR_DTYPE;
     }
     const bool d_ok = (d->d_k == 64 || d->d_k == 128) && (d->d_v == 64 || d->d_v == 128);
-    if (!d_ok || (d->qkv_dtype == GDN_F32 && d->d_k != 64)) {
-        debug("unsupported head dims for this dtype");
+    if (!d_ok) {
+        debug("unsupported head dims: d_k and d_v must be 64 or 128");
         return GDN_ERR_UNSUPPORTED;
     }
     // one chunk (64 tokens) of any packed tensor is addressed with 32-bit byte offsets
@@ -132,6 +132,7 @@ const char *gdn_status_str(int32_t s)
     case GDN_ERR_LAUNCH: return "kernel launch failed";
     case GDN_ERR_DEVICE_INPUT: return "device-side cu_seqlens / r invalid";
     case GDN_ERR_HIP: return "HIP runtime call failed";
+    case GDN_ERR_DEVICE_WAIT: return "a bounded in-kernel wait expired (results invalid)";
     default: return "unknown status";
     }
 }
@@ -216,7 +217,13 @@ int32_t gdn_device_status(const void *ws, void *stream, int32_t *status_host)
     if (hipStreamSynchronize(s) != hipSuccess) return GDN_ERR_HIP;
     int32_t v = 0;
     if (hipMemcpy(&v, ws, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return GDN_ERR_HIP;
-    *status_host = v;
+    // the kernels only OR bits into the word: reading it starts a new accumulation
+    if (v != 0 && (hipMemsetAsync(const_cast<void *>(ws), 0, sizeof(v), s) != hipSuccess ||
+                   hipStreamSynchronize(s) != hipSuccess))
+        return GDN_ERR_HIP;
+    *status_host = (v & gdn::kStatusBitInput) ? GDN_ERR_DEVICE_INPUT
+                 : (v & gdn::kStatusBitWait)  ? GDN_ERR_DEVICE_WAIT
+                                              : GDN_OK;
     return GDN_OK;
 }
 

@@ -268,6 +268,20 @@ __device__ __forceinline__ void sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Bounded wait until an LDS counter reaches `target`; an expired wait only costs wrong
+// results (flagged in the status word), never a hang.
+__device__ __forceinline__ void lds_wait_ge(const int *ctr, int target, int *fail) {
+    int spins = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > (1 << 24)) {
+            *fail = 1;
+            break;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Barrier among the prep waves only: each wave adds 1 to an LDS counter and waits
 // until every prep wave has; the target grows by NPW per use, so the counter is never
 // reset.  The wait is bounded: a wave that never arrived would only cost wrong results
@@ -289,7 +303,10 @@ __device__ __forceinline__ void prep_sync(int *ctr, int &target, int lane, int *
 
 // ---------------------------------------------------------------- LDS plan
 // Two chunk buffers (the state waves read one while the prep waves fill the other),
-// then a few words.
+// then a few words.  fp32 inputs with d_k = 128 and outputs would need 180 KB that way
+// (two 32 KB K and Q copies per buffer), more than a compute unit's 160 KB: there Q has
+// one buffer of its own, which the prep waves refill for the next chunk only once every
+// state wave has finished its Q S products of the current one (an LDS counter).
 template <int DK, int W, class P, bool WITH_O>
 struct Lds {
     typedef typename P::E E;
@@ -298,53 +315,81 @@ struct Lds {
     static constexpr int TILE = 256 * (int)sizeof(E);          // one 16x16 tile
     static constexpr int NTA = P::kBF16 ? 6 : 10;              // tile pairs (bf16) / tiles (fp32)
     static constexpr int UNIT = P::kBF16 ? 1024 : TILE;
-    // gate rows: H log2(e), e sig, b, G_last / sig, scale e sig, rho (int), then the chunk's
-    // state-scale words (renormalisation factor, sig after the chunk); 8 rows keep K at a
-    // 1 KB boundary
+    static constexpr bool Q1 = WITH_O && !P::kBF16 && DK == 128;   // single Q buffer
+    // gate rows: H (log2(e) units for bf16 inputs), e sig, b, G_last / sig, scale e sig,
+    // rho (int), the chunk's state-scale words (renormalisation factor, sig after the
+    // chunk), and for fp32 inputs the lo part of H; 8 rows keep K at a 1 KB boundary
     static constexpr int oGate = 0;
     static constexpr int oK = 8 * CH * 4;
     static constexpr int oQ = oK + CH * RBK;
     // V of the block's column range (bf16 inputs; fp32 inputs read V from global memory)
-    static constexpr int oV = oQ + (WITH_O ? CH * RBK : 0);
+    static constexpr int oV = oQ + ((WITH_O && !Q1) ? CH * RBK : 0);
     static constexpr int oA = oV + (P::kBF16 ? CH * RBV : 0);  // -A
     static constexpr int oT = oA + NTA * UNIT;                   // 4 tiles T_bb - I
     static constexpr int oPh = oT + 4 * TILE;                    // P
     static constexpr int BUF = oPh + (WITH_O ? NTA * UNIT : 0);
-    static constexpr int oMisc = 2 * BUF;
+    static constexpr int oQ1 = 2 * BUF;                          // the single Q buffer
+    static constexpr int oMisc = oQ1 + (Q1 ? CH * RBK : 0);
     static constexpr int bytes = oMisc + 64;
+    // Q rows of the chunk in buffer `buf`
+    __device__ static const char *q_rows(const char *smem, const char *buf) {
+        return Q1 ? smem + oQ1 : buf + oQ;
+    }
 };
 
 // ---------------------------------------------------------------- prep-wave pieces
 // Gates of one chunk, one token per lane: reset-aware inclusive scan of the log-gates
 // (H = sum of g since the last alpha = 0 token), e = exp(H) (0 once a reset occurred),
 // G_last = exp(H_63 - H) (0 before the chunk's last reset), rho = last reset position.
+//
+// For fp32 inputs (COMP) H is carried as an unevaluated sum h + lo of two floats: every
+// addition of the scan is a two-sum (Knuth) whose rounding error goes into lo, and the
+// differences H_i - H_j behind every G_ij are taken as (h_i - h_j) + (lo_i - lo_j),
+// accurate to the size of the difference rather than of H.  A plain fp32 scan loses
+// ulp(|H|) there: under fast decay |H| reaches a few hundred within a chunk, so G entries
+// near 1 (the last tokens' weights in the state update) are off by ~1e-5; in a partial
+// last chunk the scan even sums H_63 and H_{n-1} (equal: the rows past the window add
+// zeros) in different orders, so the newest token's weight, exactly 1, comes out as
+// 1 +- 1.5e-5 -- beyond the fp32 inputs' 1e-5 tolerance, far inside bf16's 3e-3, so
+// bf16 inputs keep the plain scan.
 struct Gates {
-    float h, e, b, l;
+    float h, lo, e, b, l;
     int rho;
 };
+template <bool COMP>
 __device__ __forceinline__ Gates gate_scan(float gv, float bv, int lane) {
     const bool reset = gv == -__builtin_inff();
-    float hv = reset ? 0.f : gv;
+    float hv = reset ? 0.f : gv, lv = 0.f;
     int seg = reset ? 1 : 0;
     int rho = reset ? lane : -1;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const float ho = __shfl_up(hv, off);
+        const float lo = COMP ? __shfl_up(lv, off) : 0.f;
         const int so = __shfl_up(seg, off);
         const int ro = __shfl_up(rho, off);
         if (lane >= off) {
-            if (!seg) hv += ho;
+            if (!seg) {
+                const float sm = hv + ho;
+                if constexpr (COMP) {
+                    const float bp = sm - hv;
+                    const float err = (hv - (sm - bp)) + (ho - bp);
+                    lv = lv + lo + err;
+                }
+                hv = sm;
+            }
             seg |= so;
             rho = ro > rho ? ro : rho;
         }
     }
-    const float hl = __shfl(hv, 63);
+    const float hl = __shfl(hv, 63), ll = COMP ? __shfl(lv, 63) : 0.f;
     const int rl = __shfl(rho, 63);
     Gates g;
     g.h = hv;
+    g.lo = lv;
     g.e = rho < 0 ? __expf(hv) : 0.f;
     g.b = bv;
-    g.l = rl <= lane ? __expf(hl - hv) : 0.f;
+    g.l = rl <= lane ? __expf(COMP ? (hl - hv) + (ll - lv) : hl - hv) : 0.f;
     g.rho = rho;
     return g;
 }
@@ -363,50 +408,66 @@ __device__ __forceinline__ Gates gate_scan(float gv, float bv, int lane) {
 template <class P, int KBK>
 struct TileIn {
     typename P::Frag kj[KBK], ki[KBK], qi[KBK];
-    f32x4 hc;
-    float hr, br;
+    f32x4 hc, lc = {0.f, 0.f, 0.f, 0.f};   // lc, lr: the lo parts of H (fp32 inputs only)
+    float hr, lr = 0.f, br;
     int rho;
 };
-template <int DK, class P, bool WITH_O, class L>
-__device__ __forceinline__ void tile_load(TileIn<P, DK / P::KB> &t, const char *buf, int ti, int tj, int lane) {
-    constexpr int KBK = DK / P::KB;
+// (tile_load and tile_mma cover the k-blocks [KB0, KB1) of d_k: all of them, or one half
+// at a time where a whole tile's fragments would not fit in registers)
+template <int DK, class P, bool WITH_O, class L, int KB0 = 0, int KB1 = DK / P::KB>
+__device__ __forceinline__ void tile_load(TileIn<P, DK / P::KB> &t, const char *buf, const char *Qb,
+                                          int ti, int tj, int lane) {
     typedef typename P::Frag F;
     const float *gH = reinterpret_cast<const float *>(buf + L::oGate);
 #pragma unroll
-    for (int kb = 0; kb < KBK; ++kb) {
+    for (int kb = KB0; kb < KB1; ++kb) {
         t.kj[kb] = frag_sw<L::RBK, F>(buf + L::oK, 16 * tj, kb, lane);
         t.ki[kb] = frag_sw<L::RBK, F>(buf + L::oK, 16 * ti, kb, lane);
-        if constexpr (WITH_O) t.qi[kb] = frag_sw<L::RBK, F>(buf + L::oQ, 16 * ti, kb, lane);
+        if constexpr (WITH_O) t.qi[kb] = frag_sw<L::RBK, F>(Qb, 16 * ti, kb, lane);
     }
     const int rr = 16 * ti + (lane & 15);
     t.hr = gH[rr];
     t.br = gH[2 * CH + rr];
     t.rho = reinterpret_cast<const int *>(gH + 5 * CH)[rr];
     t.hc = *reinterpret_cast<const f32x4 *>(gH + 16 * tj + 4 * (lane >> 4));
+    if constexpr (!P::kBF16) {
+        t.lr = gH[7 * CH + rr];
+        t.lc = *reinterpret_cast<const f32x4 *>(gH + 7 * CH + 16 * tj + 4 * (lane >> 4));
+    }
 }
-template <int DK, class P, bool WITH_O>
+template <int DK, class P, bool WITH_O, int KB0 = 0, int KB1 = DK / P::KB>
 __device__ __forceinline__ void tile_mma(const TileIn<P, DK / P::KB> &t, f32x4 &kk, f32x4 &qk) {
-    kk = f32x4{0.f, 0.f, 0.f, 0.f};
-    qk = kk;
+    if constexpr (KB0 == 0) {
+        kk = f32x4{0.f, 0.f, 0.f, 0.f};
+        qk = kk;
+    }
 #pragma unroll
-    for (int kb = 0; kb < DK / P::KB; ++kb) {
+    for (int kb = KB0; kb < KB1; ++kb) {
         kk = mma(kk, t.kj[kb], t.ki[kb]);
         if constexpr (WITH_O) qk = mma(qk, t.kj[kb], t.qi[kb]);
     }
 }
 template <int DK, class P, bool WITH_O, class L>
-__device__ __forceinline__ f32x4 tile_store(char *buf, float hr, float br, int rho, f32x4 hc, f32x4 kk,
-                                            f32x4 qk, int ti, int tj, int lane, float scale) {
+__device__ __forceinline__ f32x4 tile_store(char *buf, float hr, float lr_, float br, int rho, f32x4 hc,
+                                            f32x4 lc, f32x4 kk, f32x4 qk, int ti, int tj, int lane,
+                                            float scale) {
     const int lr = lane & 15, lg = lane >> 4;
     const int rr = 16 * ti + lr;
     f32x4 av, pv;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int c = 16 * tj + 4 * lg + e;
-        // 2^(H_i - H_j) with H in units of log2(e), of every entry, then a select: no
-        // divergent branch (the unused ones may be inf).  Off-diagonal tiles (ti > tj,
-        // known when inlined) lie wholly below the diagonal.
-        const float ex = __builtin_amdgcn_exp2f(hr - hc[e]);
+        // exp(H_i - H_j) of every entry, then a select: no divergent branch (the unused
+        // ones may be inf).  bf16 inputs: the gate row holds H log2(e), so one exp2 of
+        // the difference (its rounding, ~1e-5 relative under fast decay, is far below the
+        // bf16 tolerance); fp32 inputs: the difference of the (hi, lo) pairs, then scaled.
+        // Off-diagonal tiles (ti > tj, known when inlined) lie wholly below the diagonal.
+        float ex;
+        if constexpr (P::kBF16) {
+            ex = __builtin_amdgcn_exp2f(hr - hc[e]);
+        } else {
+            ex = __builtin_amdgcn_exp2f(((hr - hc[e]) + (lr_ - lc[e])) * 1.4426950408889634f);
+        }
         const bool below = ti > tj;
         const float gam = ((below || c <= rr) && rho <= c) ? ex : 0.f;
         av[e] = (below || c < rr) ? -br * gam * kk[e] : 0.f;
@@ -445,11 +506,18 @@ __device__ __forceinline__ f32x4 mm16(f32x4 c, f32x4 x, f32x4 y) {
     }
 }
 
-// T_bb - I for one 16x16 block from N = -A_bb (strictly lower, so N^16 = 0) in the
-// A-operand layout, as the product
-//     T = (I + A)^{-1} = (I - N)^{-1} = I + N + ... + N^15 = (I + N)(I + N^2)(I + N^4)(I + N^8),
-// every factor formed in registers on the matrix cores (fp16 operands for bf16 inputs:
-// T - I is stored in fp16 for the solve anyway); stored in fragment order (lane l: row
+// T_bb - I for one 16x16 block from N = -A_bb (strictly lower) in the A-operand layout.
+// With D the 4x4 diagonal blocks of N and E the rest (strictly block-lower),
+//     I - N = (I - G)(I - D),   G = E (I - D)^{-1},
+// and D, G are both nilpotent of order 4 (D: 4x4 strictly lower blocks; G: strictly
+// block-lower over four 4-row blocks), so
+//     T = (I + A)^{-1} = (I - D)^{-1} (I - G)^{-1} = (I + D + D^2 + D^3)(I + G + G^2 + G^3),
+// nine 16x16x16 products on the matrix cores, formed in registers (fp16 operands for
+// bf16 inputs, fp32 for fp32 inputs).  Every intermediate stays O(1) for any keys: a
+// truncated Neumann series over the whole 16x16 block, (I + N)(I + N^2)(I + N^4)(I + N^8),
+// is exact too, but its terms grow like binomial coefficients when keys are correlated
+// (|N^4| ~ 15 at a mean key cosine of 0.9, thousands for a repeated key), and fp16
+// operands then lose the result to cancellation.  Stored in fragment order (lane l: row
 // l%16, columns 4 (l/16) .. +3, at 4 l).
 template <class E>
 __device__ __forceinline__ void diag_inverse(f32x4 Nr, E *Tt, int lane) {
@@ -459,15 +527,22 @@ __device__ __forceinline__ void diag_inverse(f32x4 Nr, E *Tt, int lane) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) I4[i] = (4 * lg + i == lr) ? 1.f : 0.f;   // I, either layout
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    const f32x4 Nc = mm16<BF>(zero, Nr, I4);          // N, accumulator layout
-    const f32x4 N2c = mm16<BF>(zero, Nr, Nc), N2r = mm16<BF>(zero, Nc, Nr);
-    const f32x4 N3r = mm16<BF>(zero, N2c, Nr);        // N N^2
-    const f32x4 N4c = mm16<BF>(zero, N2r, N2c), N4r = mm16<BF>(zero, N2c, N2r);
-    const f32x4 N8c = mm16<BF>(zero, N4r, N4c);
-    const f32x4 P1r = I4 + Nr + N2r + N3r;            // (I + N)(I + N^2)
-    const f32x4 P2r = mm16<BF>(P1r, N4c, P1r);        // P1 (I + N^4)
-    const f32x4 Tr = mm16<BF>(P2r, N8c, P2r);         // P2 (I + N^8)
-    const f32x4 Tm = Tr - I4;
+    // a lane's four A-layout entries are one 4-column group: the diagonal block of its
+    // row exactly when that group is the row's
+    const bool dblk = lg == (lr >> 2);
+    const f32x4 Dr = dblk ? Nr : zero, Er = dblk ? zero : Nr;
+    const f32x4 Dc = mm16<BF>(zero, Dr, I4);          // D, accumulator layout
+    const f32x4 D2c = mm16<BF>(zero, Dr, Dc);
+    const f32x4 D3c = mm16<BF>(zero, Dr, D2c);
+    const f32x4 Dic = I4 + Dc + D2c + D3c;            // (I - D)^{-1}, accumulator layout
+    const f32x4 Gc = mm16<BF>(zero, Er, Dic);         // G
+    const f32x4 Gr = mm16<BF>(zero, Dic, Er);         // G, A-operand layout
+    const f32x4 G2c = mm16<BF>(zero, Gr, Gc);
+    const f32x4 G3c = mm16<BF>(zero, Gr, G2c);
+    const f32x4 Gi1c = Gc + G2c + G3c;                // (I - G)^{-1} - I
+    const f32x4 Dir = mm16<BF>(zero, Dic, I4);        // (I - D)^{-1}, A-operand layout
+    // T - I = ((I - D)^{-1} - I) + (I - D)^{-1} ((I - G)^{-1} - I)
+    const f32x4 Tm = mm16<BF>(Dir - I4, Gi1c, Dir);
     E *row = Tt + 4 * lane;
     if constexpr (sizeof(E) == 2) {
         *reinterpret_cast<u32x2 *>(row) = u32x2{pk_h(Tm[0], Tm[1]), pk_h(Tm[2], Tm[3])};
@@ -484,27 +559,52 @@ __device__ __forceinline__ void diag_inverse(f32x4 Nr, E *Tt, int lane) {
 // products are also kept apart from the Gram products (interleaving the two in one
 // schedule gave wrong results).
 template <int PW, int DK, class P, bool WITH_O, class L>
-__device__ __forceinline__ void prep_tiles(char *buf, int lane, float scale) {
+__device__ __forceinline__ void prep_tiles(char *buf, const char *Qb, int lane, float scale) {
     typedef typename P::E E;
     constexpr int KBK = DK / P::KB;
     constexpr int NT = PW < 4 ? 1 : PW < 7 ? 2 : 0;
     constexpr int TI[2] = {PW < 4 ? PW : PW == 4 ? 1 : PW == 5 ? 2 : 3, PW == 4 ? 2 : 3};
     constexpr int TJ[2] = {PW < 4 ? PW : PW == 4 ? 0 : PW == 5 ? 1 : 1, PW == 4 ? 0 : PW == 5 ? 0 : 2};
-    if constexpr (NT > 0) {
+    // fp32 fragments at d_k = 128 fill 96 registers per tile, more than fit next to the
+    // prefetched next chunk: there each tile is loaded and multiplied in two halves of d_k
+    constexpr bool PIPE = !(sizeof(E) == 4 && DK == 128);
+    if constexpr (NT > 0 && !PIPE) {
         TileIn<P, KBK> in;
         f32x4 kk, qk, Nr;
-        tile_load<DK, P, WITH_O, L>(in, buf, TI[0], TJ[0], lane);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            __builtin_amdgcn_sched_barrier(0);
+            tile_load<DK, P, WITH_O, L, 0, KBK / 2>(in, buf, Qb, TI[n], TJ[n], lane);
+            tile_mma<DK, P, WITH_O, 0, KBK / 2>(in, kk, qk);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_load<DK, P, WITH_O, L, KBK / 2, KBK>(in, buf, Qb, TI[n], TJ[n], lane);
+            tile_mma<DK, P, WITH_O, KBK / 2, KBK>(in, kk, qk);
+            __builtin_amdgcn_sched_barrier(0);
+            const f32x4 av = tile_store<DK, P, WITH_O, L>(buf, in.hr, in.lr, in.br, in.rho, in.hc, in.lc, kk, qk,
+                                                          TI[n], TJ[n], lane, scale);
+            if (n == 0) Nr = av;
+        }
+        if constexpr (PW < 4) {
+            __builtin_amdgcn_sched_barrier(0);
+            diag_inverse<E>(Nr, reinterpret_cast<E *>(buf + L::oT) + PW * 256, lane);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else if constexpr (NT > 0) {
+        TileIn<P, KBK> in;
+        f32x4 kk, qk, Nr;
+        tile_load<DK, P, WITH_O, L>(in, buf, Qb, TI[0], TJ[0], lane);
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             __builtin_amdgcn_sched_barrier(0);
             tile_mma<DK, P, WITH_O>(in, kk, qk);
-            const float hr = in.hr, br = in.br;
+            const float hr = in.hr, lr = in.lr, br = in.br;
             const int rho = in.rho;
-            const f32x4 hc = in.hc;
+            const f32x4 hc = in.hc, lc = in.lc;
             __builtin_amdgcn_sched_barrier(0);
-            if (n + 1 < NT) tile_load<DK, P, WITH_O, L>(in, buf, TI[n + 1], TJ[n + 1], lane);
+            if (n + 1 < NT) tile_load<DK, P, WITH_O, L>(in, buf, Qb, TI[n + 1], TJ[n + 1], lane);
             __builtin_amdgcn_sched_barrier(0);
-            const f32x4 av = tile_store<DK, P, WITH_O, L>(buf, hr, br, rho, hc, kk, qk, TI[n], TJ[n], lane, scale);
+            const f32x4 av = tile_store<DK, P, WITH_O, L>(buf, hr, lr, br, rho, hc, lc, kk, qk, TI[n], TJ[n],
+                                                          lane, scale);
             if (n == 0) Nr = av;
         }
         if constexpr (PW < 4) {
@@ -535,6 +635,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
     int64_t *gMisc = reinterpret_cast<int64_t *>(smem + L::oMisc);
     int *pctr = reinterpret_cast<int *>(smem + L::oMisc + 8);
     int *pfail = reinterpret_cast<int *>(smem + L::oMisc + 12);
+    int *qctr = reinterpret_cast<int *>(smem + L::oMisc + 16);   // Q rows released (single Q buffer)
 
     const int tid = threadIdx.x, lane0 = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -582,7 +683,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             if (b0 < 0 || b1 < b0 || b1 > a.total_tokens) bad = 1;
             if (replay && (a.r[m] < 0 || a.r[m] > b1 - b0)) bad = 1;
         }
-        if (replay && wave == 0) {   // the packed outputs must fit o_out
+        if (WITH_O && replay && wave == 0) {   // the packed outputs must fit o_out
             int64_t tot = 0;
             for (int m = lane; m < a.n_seqs; m += 64) tot += a.r[m];
 #pragma unroll
@@ -590,7 +691,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             if (tot > a.total_out) bad = 1;
         }
         bad = __syncthreads_or(bad);
-        if (tid == 0) *a.status = bad ? kStatusBadInput : kStatusOk;
+        if (tid == 0 && bad) atomicOr(a.status, kStatusBitInput);
     }
     const int64_t beg = a.cu[n], end = a.cu[n + 1];
     if (beg < 0 || end < beg || end > a.total_tokens) return;
@@ -610,6 +711,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             gMisc[0] = row0;
             *pctr = 0;
             *pfail = 0;
+            *qctr = 0;
         }
     }
     if constexpr (P::kBF16) {   // the tile pairs' upper halves are zero and never written
@@ -620,7 +722,8 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
     }
     __syncthreads();
     const int64_t orow0 = gMisc[0];
-    if (orow0 < 0 || orow0 + rn > (replay ? a.total_out : a.total_tokens)) return;
+    // output rows (and cu_out) must fit; without outputs only cu_out uses them
+    if (orow0 < 0 || orow0 + rn > ((replay && WITH_O) ? a.total_out : a.total_tokens)) return;
     if (a.cu_out && h == 0 && c_lo == 0 && tid == 0) {
         a.cu_out[n] = (int32_t)orow0;
         if (n == a.n_seqs - 1) a.cu_out[n + 1] = (int32_t)(orow0 + rn);
@@ -692,7 +795,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             const int lr = lane & 15, lg = lane >> 4;
             const char *buf = smem + (c & 1) * L::BUF;
             const char *Ks = buf + L::oK;
-            const char *Qs = buf + L::oQ;
+            const char *Qs = L::q_rows(smem, buf);
             const float *gH = reinterpret_cast<const float *>(buf + L::oGate);
             const float *gE = gH + CH, *gB = gE + CH, *gL = gB + CH, *gEs = gL + CH;
 
@@ -716,6 +819,10 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                         OT[tt] = mma(OT[tt], sh, qf);
                     }
                 }
+            }
+            if constexpr (L::Q1) {   // this chunk's Q rows are read: they may be refilled
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+                if (lane == 0) __hip_atomic_fetch_add(qctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
             // Y = b (V - e X), in place
 #pragma unroll
@@ -889,7 +996,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         const uint32_t grow = (uint32_t)a.h_v * 4u;
         u32x4 kpf[NR * VPU], qpf[NR * VPU];
         uint32_t gpf = 0, bpf = 0;
-        Gates gt = {0.f, 0.f, 0.f, 0.f, -1};
+        Gates gt = {0.f, 0.f, 0.f, 0.f, 0.f, -1};
         float sig = 1.f;                           // scale of the stored state (gate wave)
         constexpr int GW = NPW - 1;                // the wave that owns the gates
         // this lane's staging unit, the same in every chunk: its offset in a chunk's K / Q
@@ -981,7 +1088,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             if (nact == NSW) __builtin_amdgcn_s_setprio(3);
             char *buf = smem + (cc & 1) * L::BUF;
             char *Ks = buf + L::oK;
-            char *Qs = buf + L::oQ;
+            char *Qs = const_cast<char *>(L::q_rows(smem, buf));
             if (s_act) {
 #pragma unroll
                 for (int j = 0; j < NR; ++j) {
@@ -1004,8 +1111,17 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                     } else {
                         const int o = s_oa[j];
                         *reinterpret_cast<u32x4 *>(Ks + o) = kpf[j];
-                        if (WITH_O) *reinterpret_cast<u32x4 *>(Qs + o) = qpf[j];
+                        if (WITH_O && !L::Q1) *reinterpret_cast<u32x4 *>(Qs + o) = qpf[j];
                     }
+                }
+            }
+            if constexpr (L::Q1) {
+                // the single Q buffer still holds chunk cc - 1's rows until every state
+                // wave with columns has finished its Q S products of that chunk
+                lds_wait_ge(qctr, (int)cc * nact, pfail);
+                if (s_act) {
+#pragma unroll
+                    for (int j = 0; j < NR; ++j) *reinterpret_cast<u32x4 *>(Qs + s_oa[j]) = qpf[j];
                 }
             }
             if constexpr (STAGE_V) {
@@ -1029,7 +1145,12 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                 const float rn = renorm ? cand : 1.f;
                 const float sig_new = renorm ? 1.f : cand;
                 float *gH = reinterpret_cast<float *>(buf + L::oGate);
-                gH[lane] = gt.h * 1.4426950408889634f;   // log2(e)
+                if constexpr (P::kBF16) {
+                    gH[lane] = gt.h * 1.4426950408889634f;   // log2(e)
+                } else {
+                    gH[lane] = gt.h;                         // H = h + lo, natural units
+                    gH[7 * CH + lane] = gt.lo;
+                }
                 gH[CH + lane] = gt.e * sig;
                 gH[2 * CH + lane] = gt.b;
                 gH[3 * CH + lane] = gt.l / sig_new;
@@ -1046,21 +1167,21 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             prep_sync(pctr, target, lane, pfail);
 
             switch (pw) {
-            case 0: prep_tiles<0, DK, P, WITH_O, L>(buf, lane, a.scale); break;
-            case 1: prep_tiles<1, DK, P, WITH_O, L>(buf, lane, a.scale); break;
-            case 2: prep_tiles<2, DK, P, WITH_O, L>(buf, lane, a.scale); break;
-            case 3: prep_tiles<3, DK, P, WITH_O, L>(buf, lane, a.scale); break;
-            case 4: prep_tiles<4, DK, P, WITH_O, L>(buf, lane, a.scale); break;
-            case 5: prep_tiles<5, DK, P, WITH_O, L>(buf, lane, a.scale); break;
-            case 6: prep_tiles<6, DK, P, WITH_O, L>(buf, lane, a.scale); break;
+            case 0: prep_tiles<0, DK, P, WITH_O, L>(buf, Qs, lane, a.scale); break;
+            case 1: prep_tiles<1, DK, P, WITH_O, L>(buf, Qs, lane, a.scale); break;
+            case 2: prep_tiles<2, DK, P, WITH_O, L>(buf, Qs, lane, a.scale); break;
+            case 3: prep_tiles<3, DK, P, WITH_O, L>(buf, Qs, lane, a.scale); break;
+            case 4: prep_tiles<4, DK, P, WITH_O, L>(buf, Qs, lane, a.scale); break;
+            case 5: prep_tiles<5, DK, P, WITH_O, L>(buf, Qs, lane, a.scale); break;
+            case 6: prep_tiles<6, DK, P, WITH_O, L>(buf, Qs, lane, a.scale); break;
             default: break;
             }
-            if (pw == GW) gt = gate_scan(__uint_as_float(gpf), __uint_as_float(bpf), lane);
+            if (pw == GW) gt = gate_scan<!P::kBF16>(__uint_as_float(gpf), __uint_as_float(bpf), lane);
         };
 
         if (nch > 0) {
             fetch(0);
-            if (pw == GW) gt = gate_scan(__uint_as_float(gpf), __uint_as_float(bpf), lane);
+            if (pw == GW) gt = gate_scan<!P::kBF16>(__uint_as_float(gpf), __uint_as_float(bpf), lane);
             prep(0);
         }
         sync_lds();                                  // chunk 0 prepared
@@ -1068,7 +1189,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             if (c + 1 < nch) prep(c + 1);
             sync_lds();
         }
-        if (*pfail && lane == 0 && pw == 0) *a.status = kStatusBadInput;
+        if (*pfail && lane == 0 && pw == 0) atomicOr(a.status, kStatusBitWait);
     }
 }
 
@@ -1134,6 +1255,8 @@ hipError_t launch_chunk_ws(const ChunkArgs &a, int bf16, int d_k, int d_v, bool 
     } else {
         if (d_k == 64 && d_v == 64) GDN_DISPATCH(64, 64, 64, PolF32);
         if (d_k == 64 && d_v == 128) GDN_DISPATCH(64, 128, 64, PolF32);
+        if (d_k == 128 && d_v == 64) GDN_DISPATCH(128, 64, 64, PolF32);
+        if (d_k == 128 && d_v == 128) GDN_DISPATCH(128, 128, 64, PolF32);
     }
 #undef GDN_DISPATCH
     return hipErrorNotSupported;

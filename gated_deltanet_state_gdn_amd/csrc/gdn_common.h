@@ -44,7 +44,9 @@ hipError_t launch_adaptive(const float *g, const int32_t *cu, int32_t n_seqs, in
                            int64_t total_tokens, int64_t thr, int32_t r_min, int32_t r_max,
                            int32_t *r_head, int32_t *r_out, int32_t *status, hipStream_t stream);
 
-constexpr int32_t kStatusOk = 0;
-constexpr int32_t kStatusBadInput = 8;   // == GDN_ERR_DEVICE_INPUT
+// Bits of the device status word (workspace word 0).  Kernels only ever OR bits in
+// (atomically); gdn_device_status reads the word and clears it.
+constexpr int32_t kStatusBitInput = 1;   // cu_seqlens / r invalid  -> GDN_ERR_DEVICE_INPUT
+constexpr int32_t kStatusBitWait = 2;    // a bounded in-workgroup wait expired -> GDN_ERR_DEVICE_WAIT
 
 }  // namespace gdn

@@ -38,10 +38,14 @@
  * h_v % h_qk != 0, unsupported d, misaligned pointer, small workspace) return a
  * non-zero gdn_status before anything is enqueued.  A failed launch returns
  * GDN_ERR_LAUNCH.  The device-resident cu_seqlens / r are validated by the kernel
- * itself: on a bad value it records GDN_ERR_DEVICE_INPUT in the workspace status
- * word (read it with gdn_device_status), skips the offending sequences and leaves
- * their outputs unspecified.  Non-finite q/k/v/beta or g > 0 are not checked; the
- * result is then undefined and gdn_state_relerr's non-finite count exposes it.
+ * itself: on a bad value it sets a bit in the workspace's status word, skips the
+ * offending sequences and leaves their outputs unspecified.  The kernels only ever
+ * set bits in that word (atomically), never clear it: gdn_device_status reports
+ * what the calls since the previous gdn_device_status on that workspace (or since
+ * it was zero-filled) recorded, and clears it.  A new workspace must therefore be
+ * zero-filled once before its first use.  Non-finite q/k/v/beta or g > 0 are not
+ * checked; the result is then undefined and gdn_state_relerr's non-finite count
+ * exposes it.
  *
  * Arithmetic: the state is fp32 throughout.  fp32 inputs use fp32 matrix products.
  * bf16 inputs use matrix products with fp16 operands and fp32 accumulation: q and k
@@ -64,19 +68,21 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum {
     GDN_OK = 0,
     GDN_ERR_NULL = 1,          /* a required pointer is NULL */
     GDN_ERR_SHAPE = 2,         /* negative / inconsistent sizes, h_v % h_qk != 0 */
     GDN_ERR_DTYPE = 3,         /* unknown dtype code */
-    GDN_ERR_UNSUPPORTED = 4,   /* valid but not built: d_k, d_v outside {64,128}, fp32 with d_k = 128 */
+    GDN_ERR_UNSUPPORTED = 4,   /* valid but not built: d_k or d_v outside {64, 128} */
     GDN_ERR_ALIGN = 5,         /* a pointer is not 16-byte aligned */
     GDN_ERR_WORKSPACE = 6,     /* workspace missing or smaller than gdn_workspace_bytes() */
     GDN_ERR_LAUNCH = 7,        /* the HIP launch failed */
     GDN_ERR_DEVICE_INPUT = 8,  /* device-side cu_seqlens / r invalid (from gdn_device_status) */
-    GDN_ERR_HIP = 9            /* a HIP runtime call failed (gdn_device_status only) */
+    GDN_ERR_HIP = 9,           /* a HIP runtime call failed (gdn_device_status only) */
+    GDN_ERR_DEVICE_WAIT = 10   /* a bounded wait inside a workgroup expired: results invalid
+                                  (from gdn_device_status; not expected on working hardware) */
 } gdn_status;
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -89,7 +95,8 @@ typedef struct {
     int32_t o_dtype;           /* gdn_dtype of o: qkv_dtype, or GDN_F32 */
     float scale;               /* o_t = scale * S_t^T q_t */
     int64_t total_tokens;      /* T == cu_seqlens[n_seqs] (host copy) */
-    int64_t total_out_tokens;  /* rows of o_out: sum r[n] (replay) or T (prefill) */
+    int64_t total_out_tokens;  /* rows of o_out: sum r[n] (replay) or T (prefill); a replay
+                                  without o_out only needs total_out_tokens <= total_tokens */
 } gdn_desc;
 
 /* ABI version of the loaded library (GDN_ABI_VERSION). */
@@ -103,8 +110,9 @@ const char *gdn_status_str(int32_t status);
  * prefix (Tail-Replay abstract; technical summary, "Resultados"). */
 int32_t gdn_replay_len(int32_t L, double rho);
 
-/* (host) Workspace bytes a call with this descriptor needs: 256 (a status word), plus
- * n_seqs * h_v * 4 rounded up to 256 for gdn_adaptive_replay_len. */
+/* (host) Workspace bytes a call with this descriptor needs: 256 (the status word), plus
+ * n_seqs * h_v * 4 rounded up to 256 for gdn_adaptive_replay_len.  Zero-fill a new
+ * workspace once before its first use (the status word accumulates bits). */
 size_t gdn_workspace_bytes(const gdn_desc *desc);
 
 /* Tail replay: for every sequence n and v-head h, run the recurrence from S = 0 over
@@ -120,8 +128,12 @@ int32_t gdn_replay(const gdn_desc *desc, const void *q, const void *k, const voi
                    void *workspace, size_t workspace_bytes, void *stream);
 
 /* Full prefill: the recurrence over every whole sequence from S0 (NULL = zero
- * state).  o_out (nullable) has one row per token, in token order.  With S0 set to
- * a rebuilt state it continues a prefix into its suffix. */
+ * state).  This is the baseline Tail-Replay is measured against: processing the
+ * whole matched prefix again (fugumt.com page, English abstract; gist.science
+ * technical summary, "Resultados", where replay is compared with full prefill for
+ * quality and time to first token).  o_out (nullable) has one row per token, in token
+ * order.  With S0 set to a rebuilt state it continues a prefix into its unmatched
+ * suffix, the step that produces the first token after a cache hit (same section). */
 int32_t gdn_prefill(const gdn_desc *desc, const void *q, const void *k, const void *v,
                     const float *g, const float *beta, const int32_t *cu_seqlens,
                     const float *S0, float *S_out, void *o_out,
@@ -129,7 +141,12 @@ int32_t gdn_prefill(const gdn_desc *desc, const void *q, const void *k, const vo
 
 /* Error report: relerr[s] = ||S_a[s] - S_ref[s]||_F / ||S_ref[s]||_F (||S_a[s]||_F when
  * the reference is zero), fp64 accumulation; nonfinite[s] (nullable) counts the
- * non-finite entries of S_a[s].  States are d_k x d_v fp32 blocks. */
+ * non-finite entries of S_a[s].  States are d_k x d_v fp32 blocks.  It measures how
+ * far a replayed state is from the full-prefill state at the same boundary: the pages'
+ * claim is that a short recent tail approximates that state because the gated updates
+ * attenuate older inputs (fugumt.com page, English abstract), and that zeroing the state
+ * instead ("Zero-Only", relative error 1 here) degrades quality (technical summary,
+ * "Resultados"). */
 int32_t gdn_state_relerr(const float *S_a, const float *S_ref, int64_t n_states, int32_t d_k,
                          int32_t d_v, float *relerr_out, int32_t *nonfinite_out, void *stream);
 
@@ -158,9 +175,10 @@ int32_t gdn_adaptive_replay_len(const gdn_desc *desc, const float *g, const int3
                                 double eps, int32_t r_min, int32_t r_max, int32_t *r_out,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
-/* (host, synchronising) Wait for `stream` and read the status word the last compute
- * call that launched work wrote into `workspace`: GDN_OK or GDN_ERR_DEVICE_INPUT.
- * GDN_ERR_HIP if the wait or the copy failed. */
+/* (host, synchronising) Wait for `stream`, read the status word of `workspace` and
+ * clear it.  *status_host: GDN_OK, GDN_ERR_DEVICE_INPUT (a call since the previous
+ * read found a bad cu_seqlens / r) or GDN_ERR_DEVICE_WAIT.  Returns GDN_ERR_HIP if the
+ * wait, the copy or the clear failed. */
 int32_t gdn_device_status(const void *workspace, void *stream, int32_t *status_host);
 
 #ifdef __cplusplus

@@ -34,8 +34,8 @@ def test_header_declarations_are_exported():
 
 def test_version_status_and_replay_len():
     gdn, lib = _lib()
-    assert gdn.gdn_abi_version() == 1
-    for code in range(10):
+    assert gdn.gdn_abi_version() == 2
+    for code in range(11):
         assert gdn.gdn_status_str(code) not in ("unknown status", "")
     for L in (0, 1, 7, 64, 100, 2048, 8192, 32768, 12345):
         for rho in (0.0, 0.01, 0.02, 0.05, 0.07, 0.1, 0.2, 0.5, 1.0, 1.5):
@@ -70,7 +70,7 @@ def test_host_validation_codes():
     assert _replay(lib, _desc(gdn, total_out_tokens=101)) == L.GDN_ERR_SHAPE
     assert _replay(lib, _desc(gdn, d_k=96)) == L.GDN_ERR_UNSUPPORTED
     assert _replay(lib, _desc(gdn, d_v=256)) == L.GDN_ERR_UNSUPPORTED
-    assert _replay(lib, _desc(gdn, qkv_dtype=0, o_dtype=0)) == L.GDN_ERR_UNSUPPORTED  # fp32, d_k=128
+    assert _replay(lib, _desc(gdn, d_k=32)) == L.GDN_ERR_UNSUPPORTED
     assert _replay(lib, _desc(gdn, qkv_dtype=7)) == L.GDN_ERR_DTYPE
     assert _replay(lib, _desc(gdn, qkv_dtype=0, o_dtype=1, d_k=64)) == L.GDN_ERR_DTYPE
     assert _replay(lib, _desc(gdn), q=PM) == L.GDN_ERR_ALIGN

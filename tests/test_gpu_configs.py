@@ -2,10 +2,12 @@
 cannot cover every chain in seconds), in the launch configuration bench.py times.
 
   * 36-layer stack, 16 q/k heads shared by 32 v heads, d = 128, L = 32768, r = 3277:
-    replay of all layers in one call, 24 sampled (layer, v-head) chains; full
-    prefill of one layer, 4 sampled heads.
-  * 64 packed cache hits (varlen), L ~ U{1024..32768}, r = 5-10 % of L: every
-    sequence, two heads each.
+    replay of all layers in one call, every v-head of two layers plus 27 sampled
+    (layer, v-head) chains; full prefill of one layer, 8 heads (both v-heads of four
+    q/k heads).
+  * 64 packed cache hits (varlen), L ~ U{1024..32768}, r = 5-10 % of L: replay of
+    every sequence, two heads each; full prefill of the 8 shortest sequences (two heads
+    each) and the longest (one head).
   * slow decay (alpha ~ 0.9997), L = 32768: replay budgets 1/2/5/10/20 % and full
     prefill, all heads; the attenuation bound on the GPU's replay error; the alpha = 0
     variant.
@@ -43,6 +45,7 @@ def test_stack36_replay_sampled():
     rs = np.random.default_rng(7)
     pairs = [(int(l), int(h)) for l, h in zip(rs.integers(0, 36, 24), rs.integers(0, 32, 24))]
     pairs += [(0, 0), (35, 31), (17, 16)]
+    pairs += [(l, h) for l in (5, 30) for h in range(32)]          # two whole layers
     eS, eo = sampled_compare(inp, "replay", S, o, cu_out.cpu(), pairs)
     say("  sampled %d chains: relerr S %.3e  o %.3e" % (len(pairs), eS, eo))
     assert eS <= TOL and eo <= TOL
@@ -61,7 +64,7 @@ def test_stack_layer_prefill_sampled():
     say("case", w.name, "full prefill of one layer")
     S, o, _ = gpu_run(inp, "prefill")
     torch.cuda.synchronize()
-    pairs = [(0, 0), (0, 1), (0, 16), (0, 31)]
+    pairs = [(0, h) for h in (0, 1, 10, 11, 20, 21, 30, 31)]
     eS, eo = sampled_compare(inp, "prefill", S, o, None, pairs)
     say("  sampled %d chains: relerr S %.3e  o %.3e" % (len(pairs), eS, eo))
     assert eS <= TOL and eo <= TOL
@@ -75,6 +78,22 @@ def test_varlen64_replay():
     torch.cuda.synchronize()
     pairs = [(n, h) for n in range(64) for h in (n % 16, (n + 7) % 16)]
     eS, eo = sampled_compare(inp, "replay", S, o, cu_out.cpu(), pairs)
+    say("  %d chains: relerr S %.3e  o %.3e" % (len(pairs), eS, eo))
+    assert eS <= TOL and eo <= TOL
+
+
+def test_varlen64_prefill():
+    w = W.config(3)
+    inp = W.make_inputs(w, device="cuda")
+    say("case", w.name, "full prefill; sum L =", int(inp["cu_host"][-1]))
+    S, o, _ = gpu_run(inp, "prefill")
+    torch.cuda.synchronize()
+    L = np.diff(inp["cu_host"])
+    order = np.argsort(L, kind="stable")
+    pairs = [(int(n), h) for n in order[:8] for h in (int(n) % 16, (int(n) + 5) % 16)]
+    pairs.append((int(order[-1]), 3))
+    say("  sampled sequences L =", [int(L[n]) for n, _ in pairs[::2]])
+    eS, eo = sampled_compare(inp, "prefill", S, o, None, pairs)
     say("  %d chains: relerr S %.3e  o %.3e" % (len(pairs), eS, eo))
     assert eS <= TOL and eo <= TOL
 

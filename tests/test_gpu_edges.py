@@ -94,12 +94,16 @@ def test_scale():
     assert eS <= 3e-3 and eo <= 3e-3
 
 
-@pytest.mark.parametrize("dk,dv", [(64, 128)])
-def test_fp32_wide_values(dk, dv):
-    # fp32 inputs with d_v = 128 run as two column blocks per head
-    w = W.small(W.config(0), L=[300], r=[170], d_k=dk, d_v=dv)
-    inp, S, o, _, eS, eo = _case(w, "replay")
-    assert eS <= 1e-5 and eo <= 1e-5
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64), (128, 128)])
+def test_fp32_head_dims(dk, dv):
+    # fp32 inputs with d_v = 128 run as two column blocks per head; d_k = 128 keeps one Q
+    # buffer in LDS (refilled once the state waves have read it)
+    w = W.small(W.config(0), L=[300, 130, 64], r=[170, 130, 1], h_qk=2, h_v=4, d_k=dk, d_v=dv)
+    for mode in ("replay", "prefill"):
+        inp, S, o, _, eS, eo = _case(w, mode)
+        assert eS <= 1e-5 and eo <= 1e-5, (mode, eS, eo)
+    inp, S, o, _, eS, eo = _case(w, "replay", with_o=False)
+    assert o is None and eS <= 1e-5
 
 
 def test_resets_inside_and_before_window():
@@ -180,6 +184,7 @@ def test_relerr_kernel_against_host():
 
 
 def test_device_status_reports_bad_device_inputs():
+    # the kernels only set bits in the status word; gdn_device_status reads and clears it
     import gated_deltanet_state_gdn_amd as gdn
     w = W.small(W.config(1), L=[100, 50], r=[30, 20], h_qk=2, h_v=2)
     d = to_dev(W.make_inputs(w))
@@ -192,14 +197,44 @@ def test_device_status_reports_bad_device_inputs():
     gdn.gdn_replay(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], bad_r,
                    total_out_tokens=81, ws=ws)
     assert gdn.gdn_device_status(ws) == 8
+    assert gdn.gdn_device_status(ws) == 0          # cleared by the read
     bad_cu = torch.tensor([0, 120, 100], dtype=torch.int32, device="cuda")  # non-monotone
     gdn.gdn_replay(d["q"], d["k"], d["v"], d["g"], d["beta"], bad_cu, d["r"],
+                   total_out_tokens=50, ws=ws)
+    # a later good call does not erase the recorded error
+    gdn.gdn_replay(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["r"],
                    total_out_tokens=50, ws=ws)
     assert gdn.gdn_device_status(ws) == 8
     short_out = torch.tensor([30, 20], dtype=torch.int32, device="cuda")   # sum r > rows of o
     gdn.gdn_replay(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], short_out,
                    total_out_tokens=40, ws=ws)
     assert gdn.gdn_device_status(ws) == 8
+    # without outputs the sum of r is not bounded by total_out_tokens
+    gdn.gdn_replay(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], short_out,
+                   total_out_tokens=0, o_out=None, ws=ws)
+    assert gdn.gdn_device_status(ws) == 0
+
+
+def test_state_only_replay_fed_by_adaptive_lengths():
+    # r straight from gdn_adaptive_replay_len (device array, never summed on the host) and
+    # no outputs, so total_out_tokens = 0: every sequence still gets its state
+    import gated_deltanet_state_gdn_amd as gdn
+    w = W.small(W.config(1), L=[900, 300, 1500], r=[1, 1, 1], h_qk=2, h_v=4, g_mu=-3.0)
+    host = W.make_inputs(w)
+    d = to_dev(host)
+    r_dev = gdn.gdn_adaptive_replay_len(d["g"], d["cu_seqlens"], eps=1e-2, r_min=16)
+    ws = gdn.workspace(gdn.make_desc(d["q"], d["v"], 3, 0), "cuda")
+    S, o, _ = gdn.gdn_replay(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], r_dev,
+                             total_out_tokens=0, o_out=None, ws=ws)
+    assert gdn.gdn_device_status(ws) == 0 and o is None
+    r_host = r_dev.cpu().numpy().astype(np.int64)
+    say("  adaptive r", list(r_host))
+    assert (r_host >= 16).all() and (r_host < np.array(w.lengths)).all()
+    S_ref, _ = oracle.replay(host["q"], host["k"], host["v"], host["g"], host["beta"], host["cu_host"],
+                             r_host, want_o=False)
+    e = max(rel(oracle.widen(S[n, h]), S_ref[n, h]) for n in range(3) for h in range(4))
+    say("  state-only adaptive replay: relerr S %.3e" % e)
+    assert e <= TOL["bf16"]
 
 
 def test_column_slices_are_bitwise_equal_to_whole_units():
@@ -228,12 +263,13 @@ def test_column_slices_are_bitwise_equal_to_whole_units():
 def test_fast_decay_renormalises_the_stored_state(mu, dtype):
     # alpha ~ 0.88, 0.5 and 0.05 per token: the decay over a chunk reaches 2^-60 within a
     # few chunks or at once (and underflows to 0 in fp32 for mu = 3), so the kernel
-    # renormalises its stored state often; the result must not notice
-    # (fp32 at alpha ~ 0.05, far outside the workloads' alpha >= 0.9, measures 1.5e-5 on S,
-    # the same before and after the stored-state scale; it gets a 5e-5 bound)
+    # renormalises its stored state often; the result must not notice.  At mu = 3 the
+    # in-chunk log-gate sums reach a few hundred: the compensated gate scan keeps the
+    # differences behind every decay weight exact to their own size (a plain fp32 scan
+    # put 1.5e-5 on S here, the CPU model of the kernel's arithmetic pins both)
     base = W.config(0) if dtype == "f32" else W.config(1)
     w = W.small(base, L=[700, 513], r=[650, 200], h_qk=2, h_v=4, g_mu=mu, g_sigma=1.0)
-    tol = 5e-5 if (dtype == "f32" and mu > 0) else TOL[dtype]
+    tol = TOL[dtype]
     for mode in ("replay", "prefill"):
         inp, S, o, cu_out, eS, eo = _case(w, mode)
         assert eS <= tol and eo <= tol, (mode, eS, eo)

@@ -18,7 +18,14 @@ Recipe (per layer, generator seeded with ``seed``; draw order q, k, v, x_g, x_b)
   * v ~ N(0, 1), rounded to the storage dtype;
   * g = -softplus(mu + sigma * x_g), x_g ~ N(0, 1), kept fp32 (g <= 0, alpha in (0, 1]);
   * beta = sigmoid(x_b), x_b ~ N(0, 1), kept fp32;
-  * optional reset: g[p_h, h] = -inf (alpha = 0) at one position per v-head.
+  * optional reset: g[p_h, h] = -inf (alpha = 0) at one position per v-head;
+  * optional key correlation rho (``key_corr``): k = normalise(a u_h + x_k) with x_k the
+    N(0, 1) draw above, u_h a unit direction per q/k head (drawn after x_b) and
+    a^2 = rho d_k / (1 - rho), so that keys of one head have mean pairwise cosine ~rho;
+    rho = 1 gives every token of a head the same key.  Keys of a real Gated DeltaNet
+    layer pass through a short convolution and a SiLU before their L2 norm and are far
+    from independent; i.i.d. keys are the best-conditioned case of the UT transform;
+  * optional fixed beta (``beta_value``) instead of sigmoid(x_b).
 Sequence lengths, replay lengths and reset positions are drawn on the host with
 numpy's PCG64 so that they do not depend on the device the tensors are drawn on.
 Tensors are drawn with a ``torch.Generator`` on the requested device, so the same
@@ -74,6 +81,8 @@ class Workload:
     reset_heads: bool = False       # one alpha = 0 token per (sequence, v-head)
     reset_in_window: bool = False   # force that token inside the replay window
     scale: float = 1.0
+    key_corr: float = 0.0           # mean pairwise cosine of one head's keys (1: repeated key)
+    beta_value: Optional[float] = None   # fixed beta instead of sigmoid(N(0, 1))
     description: str = ""
 
     @property
@@ -158,9 +167,16 @@ def _draw_layer(w: Workload, L_total: int, seed: int, device) -> dict:
     xg = torch.randn((L_total, w.h_v), generator=gen, device=device, dtype=f32)
     xb = torch.randn((L_total, w.h_v), generator=gen, device=device, dtype=f32)
     q = q / q.norm(dim=-1, keepdim=True)
+    if w.key_corr > 0.0:
+        u = torch.randn((w.h_qk, w.d_k), generator=gen, device=device, dtype=f32)
+        u = u / u.norm(dim=-1, keepdim=True)
+        if w.key_corr >= 1.0:
+            k = k[:1].expand_as(k).clone()
+        else:
+            k = k + math.sqrt(w.key_corr * w.d_k / (1.0 - w.key_corr)) * u
     k = k / k.norm(dim=-1, keepdim=True)
     g = -torch.nn.functional.softplus(w.g_mu + w.g_sigma * xg)
-    beta = torch.sigmoid(xb)
+    beta = torch.sigmoid(xb) if w.beta_value is None else torch.full_like(xb, float(w.beta_value))
     return dict(q=_round_storage(q, w.dtype), k=_round_storage(k, w.dtype),
                 v=_round_storage(v, w.dtype), g=g.contiguous(), beta=beta.contiguous())
 
