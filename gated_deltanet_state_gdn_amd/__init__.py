@@ -20,7 +20,7 @@ from ._lib import (GDN_BF16, GDN_F32, GdnDesc, GdnError, GDN_ERR_DEVICE_INPUT, G
                    LIB_PATH, load)
 
 __all__ = ["gdn_replay", "gdn_prefill", "gdn_state_relerr", "gdn_device_status",
-           "gdn_adaptive_replay_len",
+           "gdn_adaptive_replay_len", "gdn_adaptive_replay_len_static",
            "gdn_workspace_bytes", "gdn_replay_len", "gdn_status_str", "gdn_abi_version",
            "GdnError", "make_desc", "workspace", "LIB_PATH", "load"]
 
@@ -168,4 +168,20 @@ def gdn_adaptive_replay_len(g, cu_seqlens, *, eps: float, r_min: int = 0, r_max:
                                        int(r_min), int(r_max), _ptr(r_out), _ptr(ws), ws.numel(),
                                        _stream(stream))
     _check(code, "gdn_adaptive_replay_len")
+    return r_out
+
+
+def gdn_adaptive_replay_len_static(g, cu_seqlens, *, eps: float, r_min: int = 0,
+                                   r_max: int = 2**31 - 1, r_out=None, stream=None):
+    """gdn_adaptive_replay_len without a workspace (the library's static device scratch;
+    see include/gdn.h).  ``r_out`` must be given by callers that cannot allocate."""
+    lib = load()
+    n = int(cu_seqlens.shape[0]) - 1
+    d = GdnDesc()
+    d.n_seqs, d.h_v, d.total_tokens = n, int(g.shape[1]), int(g.shape[0])
+    if r_out is None:
+        r_out = torch.empty(max(n, 0), dtype=torch.int32, device=g.device)
+    code = lib.gdn_adaptive_replay_len_static(ctypes.byref(d), _ptr(g), _ptr(cu_seqlens), float(eps),
+                                              int(r_min), int(r_max), _ptr(r_out), _stream(stream))
+    _check(code, "gdn_adaptive_replay_len_static")
     return r_out

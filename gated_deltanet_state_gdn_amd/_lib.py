@@ -9,14 +9,14 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
 GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 GDN_ERR_ALIGN, GDN_ERR_WORKSPACE, GDN_ERR_LAUNCH, GDN_ERR_DEVICE_INPUT, GDN_ERR_HIP = 5, 6, 7, 8, 9
-GDN_ERR_DEVICE_WAIT = 10
+GDN_ERR_DEVICE_WAIT, GDN_ERR_SCRATCH = 10, 11
 GDN_F32, GDN_BF16 = 0, 1
 ABI_VERSION = 2
 
 # every symbol include/gdn.h declares
 EXPORTS = ("gdn_abi_version", "gdn_status_str", "gdn_replay_len", "gdn_workspace_bytes",
            "gdn_replay", "gdn_prefill", "gdn_state_relerr", "gdn_device_status",
-           "gdn_adaptive_replay_len")
+           "gdn_adaptive_replay_len", "gdn_adaptive_replay_len_static")
 
 
 class GdnDesc(ctypes.Structure):
@@ -65,6 +65,8 @@ def load() -> ctypes.CDLL:
     lib.gdn_device_status.restype = i32
     lib.gdn_adaptive_replay_len.argtypes = [dptr, vp, vp, ctypes.c_double, i32, i32, vp, vp, sz, vp]
     lib.gdn_adaptive_replay_len.restype = i32
+    lib.gdn_adaptive_replay_len_static.argtypes = [dptr, vp, vp, ctypes.c_double, i32, i32, vp, vp]
+    lib.gdn_adaptive_replay_len_static.restype = i32
     if lib.gdn_abi_version() != ABI_VERSION:
         raise ImportError("libgdn.so ABI version mismatch")
     _lib = lib

@@ -21,9 +21,21 @@
 // tokens per step (8 per lane, in flight together), with a wavefront prefix sum,
 // and stops at the first crossing.  Pass 2: one workgroup takes the maximum over
 // heads, clamps it, validates cu_seqlens and sets the status word's bad-input bit.
+#include <atomic>
+#include <mutex>
+
 #include "gdn_common.h"
 
 namespace gdn {
+
+// Device memory of the allocation-free variant (gdn_adaptive_replay_len_static): word 0
+// is its status word, words [kStaticPad, kStaticPad + kStaticHeads) its per-head
+// lengths.  Every GPU the library runs on holds its own copy until the process ends.
+// Host code never uses this name as an address: static_scratch() returns the device
+// address, looked up once per device.
+constexpr int kStaticPad = 64;                      // status word, padded to 256 bytes
+static __device__ __align__(256) int32_t scratch[kStaticPad + kStaticHeads];
+
 namespace {
 
 constexpr int U = 8;                              // tokens per lane per step
@@ -132,6 +144,37 @@ __global__ void __launch_bounds__(256) adaptive_reduce_kernel(const int32_t *cu,
 }
 
 }  // namespace
+
+// Device address of `scratch` on the current device, looked up on the first call with
+// that device current and kept per device; nullptr if the lookup fails.
+static int32_t *static_scratch()
+{
+    static std::mutex mu;
+    static int32_t *addr[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        addr[dev] = static_cast<int32_t *>(p);
+    }
+    return addr[dev];
+}
+
+hipError_t launch_adaptive_static(const float *g, const int32_t *cu, int32_t n_seqs, int32_t h_v,
+                                  int64_t total_tokens, int64_t thr, int32_t r_min, int32_t r_max,
+                                  int32_t *r_out, hipStream_t stream)
+{
+    if ((int64_t)n_seqs * h_v > kStaticHeads) return hipErrorInvalidValue;
+    int32_t *base = static_scratch();
+    if (!base) return hipErrorInvalidSymbol;
+    // the per-head lengths are all written by the first kernel before the second reads
+    // them, so nothing needs clearing; the status word only collects bits nobody reads
+    // (a bad cu_seqlens shows as r_out[n] = 0)
+    return launch_adaptive(g, cu, n_seqs, h_v, total_tokens, thr, r_min, r_max, base + kStaticPad,
+                           r_out, base, stream);
+}
 
 hipError_t launch_adaptive(const float *g, const int32_t *cu, int32_t n_seqs, int32_t h_v,
                            int64_t total_tokens, int64_t thr, int32_t r_min, int32_t r_max,

@@ -133,6 +133,7 @@ const char *gdn_status_str(int32_t s)
     case GDN_ERR_DEVICE_INPUT: return "device-side cu_seqlens / r invalid";
     case GDN_ERR_HIP: return "HIP runtime call failed";
     case GDN_ERR_DEVICE_WAIT: return "a bounded in-kernel wait expired (results invalid)";
+    case GDN_ERR_SCRATCH: return "request larger than the library's static device scratch";
     default: return "unknown status";
     }
 }
@@ -207,6 +208,32 @@ int32_t gdn_adaptive_replay_len(const gdn_desc *d, const float *g, const int32_t
                                               thr, r_min, r_max, scratch, r_out,
                                               reinterpret_cast<int32_t *>(ws),
                                               reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+int32_t gdn_adaptive_replay_len_static(const gdn_desc *d, const float *g, const int32_t *cu_seqlens,
+                                       double eps, int32_t r_min, int32_t r_max, int32_t *r_out,
+                                       void *stream)
+{
+    if (!d) return GDN_ERR_NULL;
+    if (d->n_seqs < 0 || d->h_v <= 0 || d->total_tokens < 0 || d->total_tokens > 0x7fffffffLL ||
+        r_min < 0 || r_max < r_min || !(eps > 0.0)) {
+        debug("adaptive replay length: bad sizes, clamp range or eps");
+        return GDN_ERR_SHAPE;
+    }
+    if ((int64_t)d->n_seqs * d->h_v > gdn::kStaticHeads) {
+        debug("allocation-free adaptive replay length: n_seqs * h_v exceeds the static scratch (65536)");
+        return GDN_ERR_SCRATCH;
+    }
+    if (!cu_seqlens || !r_out || (d->total_tokens > 0 && !g)) return GDN_ERR_NULL;
+    if (!aligned16(g) || ((uintptr_t)cu_seqlens & 3u) || ((uintptr_t)r_out & 3u)) return GDN_ERR_ALIGN;
+    if (d->n_seqs == 0) return GDN_OK;
+    int64_t thr = 0;
+    if (eps < 1.0) thr = (int64_t)floor(log(eps) * 4294967296.0);
+    const hipError_t e = gdn::launch_adaptive_static(g, cu_seqlens, d->n_seqs, d->h_v, d->total_tokens,
+                                                     thr, r_min, r_max, r_out,
+                                                     reinterpret_cast<hipStream_t>(stream));
+    if (e == hipErrorInvalidSymbol) return GDN_ERR_HIP;
     return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 

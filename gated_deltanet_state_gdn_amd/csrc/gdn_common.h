@@ -44,6 +44,15 @@ hipError_t launch_adaptive(const float *g, const int32_t *cu, int32_t n_seqs, in
                            int64_t total_tokens, int64_t thr, int32_t r_min, int32_t r_max,
                            int32_t *r_head, int32_t *r_out, int32_t *status, hipStream_t stream);
 
+// The same with the per-head lengths and the status word in the library's static device
+// scratch (no workspace, no allocation).  n_seqs * h_v must be <= kStaticHeads
+// (hipErrorInvalidValue otherwise); hipErrorInvalidSymbol if the scratch's device address
+// cannot be looked up.
+constexpr int64_t kStaticHeads = 65536;
+hipError_t launch_adaptive_static(const float *g, const int32_t *cu, int32_t n_seqs, int32_t h_v,
+                                  int64_t total_tokens, int64_t thr, int32_t r_min, int32_t r_max,
+                                  int32_t *r_out, hipStream_t stream);
+
 // Bits of the device status word (workspace word 0).  Kernels only ever OR bits in
 // (atomically); gdn_device_status reads the word and clears it.
 constexpr int32_t kStatusBitInput = 1;   // cu_seqlens / r invalid  -> GDN_ERR_DEVICE_INPUT

@@ -81,8 +81,10 @@ typedef enum {
     GDN_ERR_LAUNCH = 7,        /* the HIP launch failed */
     GDN_ERR_DEVICE_INPUT = 8,  /* device-side cu_seqlens / r invalid (from gdn_device_status) */
     GDN_ERR_HIP = 9,           /* a HIP runtime call failed (gdn_device_status only) */
-    GDN_ERR_DEVICE_WAIT = 10   /* a bounded wait inside a workgroup expired: results invalid
+    GDN_ERR_DEVICE_WAIT = 10,  /* a bounded wait inside a workgroup expired: results invalid
                                   (from gdn_device_status; not expected on working hardware) */
+    GDN_ERR_SCRATCH = 11       /* request larger than the static device scratch of an
+                                  allocation-free entry point */
 } gdn_status;
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -174,6 +176,21 @@ int32_t gdn_state_relerr(const float *S_a, const float *S_ref, int64_t n_states,
 int32_t gdn_adaptive_replay_len(const gdn_desc *desc, const float *g, const int32_t *cu_seqlens,
                                 double eps, int32_t r_min, int32_t r_max, int32_t *r_out,
                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Allocation-free gdn_adaptive_replay_len, for callers that cannot allocate device
+ * memory or take a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments and result as
+ * gdn_adaptive_replay_len minus the workspace: its per-head lengths live in the
+ * library's own static device scratch, 65536 int32 per GPU (plus a 256-byte status
+ * block), held until the process ends; it calls no allocator.  Limit: n_seqs * h_v <=
+ * 65536, else GDN_ERR_SCRATCH before anything is enqueued.  All calls on one GPU share
+ * that scratch: calls that overlap on one GPU (concurrent streams, threads) race and give
+ * undefined r_out; calls ordered on one stream are fine.  A bad device cu_seqlens shows
+ * as r_out[n] = 0 for the sequences concerned (there is no status word to read).
+ * GDN_ERR_HIP if the scratch's device address cannot be looked up. */
+int32_t gdn_adaptive_replay_len_static(const gdn_desc *desc, const float *g,
+                                       const int32_t *cu_seqlens, double eps, int32_t r_min,
+                                       int32_t r_max, int32_t *r_out, void *stream);
 
 /* (host, synchronising) Wait for `stream`, read the status word of `workspace` and
  * clear it.  *status_host: GDN_OK, GDN_ERR_DEVICE_INPUT (a call since the previous

@@ -35,7 +35,7 @@ def test_header_declarations_are_exported():
 def test_version_status_and_replay_len():
     gdn, lib = _lib()
     assert gdn.gdn_abi_version() == 2
-    for code in range(11):
+    for code in range(12):
         assert gdn.gdn_status_str(code) not in ("unknown status", "")
     for L in (0, 1, 7, 64, 100, 2048, 8192, 32768, 12345):
         for rho in (0.0, 0.01, 0.02, 0.05, 0.07, 0.1, 0.2, 0.5, 1.0, 1.5):
@@ -105,3 +105,21 @@ def test_relerr_and_status_validation():
 def test_workspace_size():
     gdn, lib = _lib()
     assert gdn.gdn_workspace_bytes(_desc(gdn)) >= 256
+
+
+def test_allocation_free_adaptive_rejects_oversized_requests():
+    # n_seqs * h_v beyond the 65536 per-head slots of the static scratch is refused on the
+    # host, before any device call
+    gdn, lib = _lib()
+    L = gdn._lib
+    d = gdn._lib.GdnDesc()
+    d.n_seqs, d.h_v, d.total_tokens = 2049, 32, 4096
+    assert lib.gdn_adaptive_replay_len_static(ctypes.byref(d), P, P, 1e-3, 0, 100, P, None) == L.GDN_ERR_SCRATCH
+    d.n_seqs, d.h_v = 1, 65537
+    assert lib.gdn_adaptive_replay_len_static(ctypes.byref(d), P, P, 1e-3, 0, 100, P, None) == L.GDN_ERR_SCRATCH
+    d.n_seqs, d.h_v = 2, 4
+    assert lib.gdn_adaptive_replay_len_static(ctypes.byref(d), P, P, -1.0, 0, 100, P, None) == L.GDN_ERR_SHAPE
+    assert lib.gdn_adaptive_replay_len_static(ctypes.byref(d), P, None, 1e-3, 0, 100, P, None) == L.GDN_ERR_NULL
+    assert lib.gdn_adaptive_replay_len_static(ctypes.byref(d), PM, P, 1e-3, 0, 100, P, None) == L.GDN_ERR_ALIGN
+    d.n_seqs = 0
+    assert lib.gdn_adaptive_replay_len_static(ctypes.byref(d), P, P, 1e-3, 0, 100, P, None) == L.GDN_OK
