@@ -554,15 +554,17 @@ __device__ __forceinline__ void diag_inverse(f32x4 Nr, E *Tt, int lane) {
 // The Gram tiles of prep wave PW: waves 0..3 own diagonal block PW (formed, then inverted
 // in registers); waves 4..6 two off-diagonal tiles each; wave 7 none (it owns the gates).
 //   wave 4: (1,0) (2,0)   wave 5: (2,1) (3,0)   wave 6: (3,1) (3,2)
+// In a column-slice workgroup, whose state waves without columns would only wait, three
+// of them form the second tiles of waves 4..6 instead (NT1 = 1 there; see help_tile).
 // Software-pipelined: the next tile's fragments are in flight while the current one is
 // finished.  The stages are kept in order with scheduling barriers; the inverse's
 // products are also kept apart from the Gram products (interleaving the two in one
 // schedule gave wrong results).
-template <int PW, int DK, class P, bool WITH_O, class L>
+template <int PW, int DK, class P, bool WITH_O, class L, int NT1 = 2>
 __device__ __forceinline__ void prep_tiles(char *buf, const char *Qb, int lane, float scale) {
     typedef typename P::E E;
     constexpr int KBK = DK / P::KB;
-    constexpr int NT = PW < 4 ? 1 : PW < 7 ? 2 : 0;
+    constexpr int NT = PW < 4 ? 1 : PW < 7 ? NT1 : 0;
     constexpr int TI[2] = {PW < 4 ? PW : PW == 4 ? 1 : PW == 5 ? 2 : 3, PW == 4 ? 2 : 3};
     constexpr int TJ[2] = {PW < 4 ? PW : PW == 4 ? 0 : PW == 5 ? 1 : 1, PW == 4 ? 0 : PW == 5 ? 0 : 2};
     // fp32 fragments at d_k = 128 fill 96 registers per tile, more than fit next to the
@@ -615,8 +617,34 @@ __device__ __forceinline__ void prep_tiles(char *buf, const char *Qb, int lane, 
     }
 }
 
+// One off-diagonal Gram tile (TI > TJ) formed by a helper wave: the second tile of prep
+// wave 4, 5 or 6 (HW = 0, 1, 2), the same arithmetic as there.
+template <int HW, int DK, class P, bool WITH_O, class L>
+__device__ __forceinline__ void help_tile(char *buf, const char *Qb, int lane, float scale) {
+    typedef typename P::E E;
+    constexpr int KBK = DK / P::KB;
+    constexpr int TI = HW == 2 ? 3 : HW + 2, TJ = HW == 2 ? 2 : 0;
+    constexpr bool PIPE = !(sizeof(E) == 4 && DK == 128);
+    TileIn<P, KBK> in;
+    f32x4 kk, qk;
+    if constexpr (PIPE) {
+        tile_load<DK, P, WITH_O, L>(in, buf, Qb, TI, TJ, lane);
+        tile_mma<DK, P, WITH_O>(in, kk, qk);
+    } else {
+        tile_load<DK, P, WITH_O, L, 0, KBK / 2>(in, buf, Qb, TI, TJ, lane);
+        tile_mma<DK, P, WITH_O, 0, KBK / 2>(in, kk, qk);
+        __builtin_amdgcn_sched_barrier(0);
+        tile_load<DK, P, WITH_O, L, KBK / 2, KBK>(in, buf, Qb, TI, TJ, lane);
+        tile_mma<DK, P, WITH_O, KBK / 2, KBK>(in, kk, qk);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    tile_store<DK, P, WITH_O, L>(buf, in.hr, in.lr, in.br, in.rho, in.hc, in.lc, kk, qk, TI, TJ, lane, scale);
+}
+
 // ---------------------------------------------------------------- kernel
-template <int DK, int DV, int W, class P, bool WITH_O>
+// HELP: every block is a column slice in which at least three state waves have no columns
+// (the launcher guarantees it); those form three of the Gram tiles (help_tile).
+template <int DK, int DV, int W, class P, bool WITH_O, bool HELP>
 __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(ChunkArgs a)
 {
     constexpr int NSW = W / 16;            // state waves: one 16-column tile of S each
@@ -657,12 +685,12 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         int64_t b = blockIdx.x;
         if (b < a.n_full) {
             if ((a.n_full & 7) == 0) b = (b & 7) * (a.n_full >> 3) + (b >> 3);
-            unit = b;
+            unit = a.unit0 + b;
         } else {
             const int64_t m = nblk - a.n_full;
             b -= a.n_full;
             if ((m & 7) == 0) b = (b & 7) * (m >> 3) + (b >> 3);
-            unit = a.n_full + (b >> a.split);
+            unit = a.unit0 + a.n_full + (b >> a.split);
             slice = (int)(b & ((1 << a.split) - 1));
             ncols = W >> a.split;
         }
@@ -735,10 +763,37 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
     const E *vg = reinterpret_cast<const E *>(a.v);
     const int64_t sbase = ((int64_t)n * a.h_v + h) * DK * DV;
 
+    // HELP: three state waves without columns form the second Gram tiles of prep waves
+    // 4..6, which shortens the prep waves' chain (it sets the chunk period when only a few
+    // state waves have columns)
     if (is_state && wave >= nact) {
-        // a state wave without columns (a split block): only the state waves' barriers
-        sync_lds();
-        for (int64_t c = 0; c < nch; ++c) sync_lds();
+        const int hw = wave - nact;
+        if (HELP && hw < 3) {
+            int htarget = 0;
+            auto help = [&](int64_t cc) {
+                int lane = lane0;
+                asm volatile("" : "+v"(lane));
+                htarget += NPW;                     // after the prep waves' staging of chunk cc
+                lds_wait_ge(pctr, htarget, pfail);
+                char *buf = smem + (cc & 1) * L::BUF;
+                const char *Qb = L::q_rows(smem, buf);
+                switch (hw) {
+                case 0: help_tile<0, DK, P, WITH_O, L>(buf, Qb, lane, a.scale); break;
+                case 1: help_tile<1, DK, P, WITH_O, L>(buf, Qb, lane, a.scale); break;
+                default: help_tile<2, DK, P, WITH_O, L>(buf, Qb, lane, a.scale); break;
+                }
+            };
+            if (nch > 0) help(0);
+            sync_lds();                              // chunk 0 prepared
+            for (int64_t c = 0; c < nch; ++c) {
+                if (c + 1 < nch) help(c + 1);
+                sync_lds();
+            }
+        } else {
+            // a state wave without columns (a split block): only the state waves' barriers
+            sync_lds();
+            for (int64_t c = 0; c < nch; ++c) sync_lds();
+        }
     } else if (is_state) {
         // =====================================================================
         // state waves
@@ -1171,9 +1226,9 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             case 1: prep_tiles<1, DK, P, WITH_O, L>(buf, Qs, lane, a.scale); break;
             case 2: prep_tiles<2, DK, P, WITH_O, L>(buf, Qs, lane, a.scale); break;
             case 3: prep_tiles<3, DK, P, WITH_O, L>(buf, Qs, lane, a.scale); break;
-            case 4: prep_tiles<4, DK, P, WITH_O, L>(buf, Qs, lane, a.scale); break;
-            case 5: prep_tiles<5, DK, P, WITH_O, L>(buf, Qs, lane, a.scale); break;
-            case 6: prep_tiles<6, DK, P, WITH_O, L>(buf, Qs, lane, a.scale); break;
+            case 4: prep_tiles<4, DK, P, WITH_O, L, HELP ? 1 : 2>(buf, Qs, lane, a.scale); break;
+            case 5: prep_tiles<5, DK, P, WITH_O, L, HELP ? 1 : 2>(buf, Qs, lane, a.scale); break;
+            case 6: prep_tiles<6, DK, P, WITH_O, L, HELP ? 1 : 2>(buf, Qs, lane, a.scale); break;
             default: break;
             }
             if (pw == GW) gt = gate_scan<!P::kBF16>(__uint_as_float(gpf), __uint_as_float(bpf), lane);
@@ -1206,7 +1261,7 @@ int64_t resident_slots()
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per, reinterpret_cast<const void *>(&gdn_chunk_ws_kernel<DK, DV, W, P, WITH_O>),
+            &per, reinterpret_cast<const void *>(&gdn_chunk_ws_kernel<DK, DV, W, P, WITH_O, false>),
             64 * (W / 16 + NPW), 0) != hipSuccess)
         return 0;
     v = (int64_t)cus * (per > 0 ? per : 1);
@@ -1234,10 +1289,31 @@ hipError_t launch_t(const ChunkArgs &a0, hipStream_t stream)
             a.split = sp;
         }
     }
+    a.unit0 = 0;
     const int64_t nblk = a.n_full + ((units - a.n_full) << a.split);
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gdn_chunk_ws_kernel<DK, DV, W, P, WITH_O>), dim3((unsigned)nblk),
-                       dim3(64 * (W / 16 + NPW)), 0, stream, a);
+    // slices in which at least three state waves have no columns go to a second launch
+    // whose idle state waves help with the Gram tiles
+    const bool help = a.split > 0 && W / 16 - ((W >> a.split) / 16) >= 3;
+    if (!help) {
+        hipLaunchKernelGGL((gdn_chunk_ws_kernel<DK, DV, W, P, WITH_O, false>), dim3((unsigned)nblk),
+                           dim3(64 * (W / 16 + NPW)), 0, stream, a);
+        return hipGetLastError();
+    }
+    if (a.n_full > 0) {   // the whole units
+        ChunkArgs w = a;
+        w.split = 0;
+        hipLaunchKernelGGL((gdn_chunk_ws_kernel<DK, DV, W, P, WITH_O, false>), dim3((unsigned)a.n_full),
+                           dim3(64 * (W / 16 + NPW)), 0, stream, w);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    ChunkArgs sl = a;     // the slices
+    sl.unit0 = a.n_full;
+    sl.n_full = 0;
+    hipLaunchKernelGGL((gdn_chunk_ws_kernel<DK, DV, W, P, WITH_O, true>),
+                       dim3((unsigned)((units - a.n_full) << a.split)), dim3(64 * (W / 16 + NPW)), 0, stream,
+                       sl);
     return hipGetLastError();
 }
 
