@@ -5,7 +5,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgdn.so")
+# GDN_LIB_PATH selects another build of the same library (e.g. a host-sanitized one)
+LIB_PATH = os.environ.get("GDN_LIB_PATH") or os.path.join(_HERE, "libgdn.so")
 
 GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 GDN_ERR_ALIGN, GDN_ERR_WORKSPACE, GDN_ERR_LAUNCH, GDN_ERR_DEVICE_INPUT, GDN_ERR_HIP = 5, 6, 7, 8, 9

@@ -58,6 +58,47 @@ def build(jobs: int = 4, verbose: bool = True) -> str:
     return LIB
 
 
+# Host-side sanitizers for the argument validation in gdn_api.hip: only host code is
+# instrumented (each -fsanitize= follows -Xarch_host); device code is built as usual.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_host_sanitized(out_dir: str = os.path.join(BUILD, "hostsan")) -> str:
+    """libgdn with an ASan+UBSan-instrumented gdn_api.hip, for CPU-only validation tests.
+
+    The process that loads it must preload clang's ASan runtime
+    (``clang_asan_runtime()``).  The other objects are the regular build's.
+    """
+    os.makedirs(out_dir, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        if src == "gdn_api.hip":
+            continue
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        if not os.path.exists(obj) or os.path.getmtime(obj) < os.path.getmtime(os.path.join(CSRC, src)):
+            os.makedirs(BUILD, exist_ok=True)
+            _compile(src)
+        objs.append(obj)
+    api = os.path.join(out_dir, "gdn_api.o")
+    subprocess.check_call([hipcc()] + flags() + HOST_SANITIZE +
+                          ["-c", os.path.join(CSRC, "gdn_api.hip"), "-o", api])
+    lib = os.path.join(out_dir, "libgdn_hostsan.so")
+    subprocess.check_call([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", lib, api] + objs)
+    return lib
+
+
+def clang_asan_runtime() -> str:
+    """Path of the ROCm clang's shared ASan runtime (includes the UBSan handlers)."""
+    root = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "lib", "clang")
+    for ver in sorted(os.listdir(root), reverse=True):
+        p = os.path.join(root, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(p):
+            return p
+    raise RuntimeError("clang ASan runtime not found under " + root)
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=4)

@@ -23,6 +23,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
+import re
 import subprocess
 import threading
 
@@ -30,7 +31,11 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdn_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# GDN_ORACLE_SANITIZE (e.g. "address,undefined" or "thread") selects a separately
+# built, instrumented copy; the process must then preload gcc's matching runtime.
+_SANITIZE = os.environ.get("GDN_ORACLE_SANITIZE", "").strip()
+_LIB_PATH = os.path.join(_HERE, "liboracle.so" if not _SANITIZE else
+                         "liboracle_%s.so" % re.sub(r"[^a-z]+", "_", _SANITIZE))
 _lib = None
 _lock = threading.Lock()
 
@@ -40,8 +45,10 @@ def build(force: bool = False) -> str:
     if force or not os.path.exists(_LIB_PATH) or \
             os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        extra = [] if not _SANITIZE else ["-fsanitize=" + _SANITIZE, "-fno-sanitize-recover=all",
+                                          "-fno-omit-frame-pointer", "-g"]
         subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread",
-                               "-fno-fast-math", "-o", tmp, _SRC, "-lm"])
+                               "-fno-fast-math"] + extra + ["-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
