@@ -8,7 +8,9 @@ gdn_replay call over the 36 layers packed as 36 sequences.
 
 Metric: replayed tokens per second per GDN layer (= 36 * r / step time) and the
 state-rebuild time per layer (step time / 36).  Inputs are resident in HBM when the
-timed region starts.
+timed region starts.  A workload of under 1 GiB per step (the single-layer ones) would
+be served from the 256 MB MALL on repeated steps, so it is timed step by step after a
+1 GiB write, and its step time is the median per-launch time.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg2|cfg1|cfg4|cfg3]
 
@@ -109,20 +111,32 @@ def main():
     if status != 0:
         raise RuntimeError("device status %d" % status)
 
+    # A workload whose bytes fit in the 256 MB MALL several times over would be served
+    # from it on repeated steps: such workloads flush it before every step and take the
+    # step time from the per-launch events (median) instead of the wall clock.
+    flush = MallFlush(dev)
+    cold = algorithmic_bytes(w, tot, n_seqs, with_o) < (1 << 30)
+
     # timed region: K steps, per-launch events on the launch stream
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if cold:
+            flush()
         ev[i][0].record(stream)
         step()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     launch_ms = [a.elapsed_time(b) for a, b in ev]
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = float(np.median(launch_ms)) if cold else wall * 1e3 / args.steps
     kern_ms = float(np.mean(launch_ms))
+    launch_stats = {"mean": kern_ms, "median": float(np.median(launch_ms)),
+                    "p10": float(np.percentile(launch_ms, 10)),
+                    "p90": float(np.percentile(launch_ms, 90)),
+                    "min": float(np.min(launch_ms)), "max": float(np.max(launch_ms))}
 
     layers = n_seqs if w.layers > 1 else 1
     # per GDN layer: a layer rebuilds r tokens in t_step / layers, so its throughput is
@@ -149,6 +163,8 @@ def main():
                    "r": list(w.replay)[:4], "replayed_tokens_per_step": tot, "with_o": with_o,
                    "state": "fp32"},
         "rebuild_us_per_layer": kern_ms * 1e3 / layers,
+        "launch_ms": launch_stats,
+        "mall_flushed_per_step": cold,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profile(kern_ms),
                      "algorithmic_bytes_per_launch": abytes, "kernel_ms": kern_ms,
@@ -177,15 +193,7 @@ def main():
             f1 = lambda: gdn.gdn_replay(q[sl], k[sl], v[sl], g[sl], beta[sl], cu1, r1,
                                         total_out_tokens=int(inp["r_host"][0]), S_out=S1, o_out=o1,
                                         ws=ws, scale=w.scale, stream=stream)
-            for _ in range(3):
-                f1()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(10):
-                f1()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            out["single_layer_call_us"] = e0.elapsed_time(e1) * 1e3 / 10
+            out["single_layer_call_us"] = _time_cold(f1, stream, 10, flush) * 1e3
         # full prefill of the same packed prefixes (the baseline the replay replaces)
         Sp = torch.empty_like(S)
         op = torch.empty((int(q.shape[0]), w.h_v, w.d_v), dtype=q.dtype, device=dev) if with_o else None
@@ -211,13 +219,46 @@ def main():
         out["adaptive_replay_len"] = adaptive_leg(w, inp, gdn, stream, ws, Sp, layers, with_o)
         out["transfer_overlap"] = overlap_leg(step, stream, kern_ms)
         if not args.no_sweep:
-            out["gate_sweep"] = gate_sweep_leg(gdn, stream, with_o)
+            out["gate_sweep"] = gate_sweep_leg(gdn, stream, with_o, flush)
         del Sp
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, with_o, args.cpu_seconds)
 
     print(json.dumps(out), flush=True)
+
+
+class MallFlush:
+    """Writes 1 GiB (four times the 256 MB last-level MALL) so that the next timed call
+    finds none of its inputs in the cache."""
+
+    def __init__(self, device, nbytes=1 << 30):
+        import torch
+        self.buf = torch.empty(nbytes // 4, dtype=torch.int32, device=device)
+        self.k = 0
+
+    def __call__(self):
+        self.k += 1
+        self.buf.fill_(self.k)
+
+
+def _time_cold(fn, stream, reps, flush):
+    """Median time (ms) of `reps` single calls, each after a MALL flush, with events on
+    the launch stream around the call only."""
+    import numpy as np
+    import torch
+    fn()
+    ts = []
+    for _ in range(reps):
+        with torch.cuda.stream(stream):
+            flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts))
 
 
 def _time(fn, stream, reps):
@@ -306,10 +347,11 @@ def adaptive_leg(w, inp, gdn, stream, ws, S_full, layers, with_o, eps=1e-3):
                                "nonfinite": int(nf.sum())}}
 
 
-def gate_sweep_leg(gdn, stream, with_o):
+def gate_sweep_leg(gdn, stream, with_o, flush):
     """Slow-decay layer (16 heads, d = 128, bf16, L = 32768, alpha ~ 0.9997), without and
     with one alpha = 0 token per head: replay time and error against full prefill at the
-    replay budgets 1, 2, 5, 10 and 20 %, and the full prefill itself."""
+    replay budgets 1, 2, 5, 10 and 20 %, and the full prefill itself (each call timed
+    alone after a MALL flush, median)."""
     import torch
     import workloads as W
     res = {}
@@ -319,8 +361,8 @@ def gate_sweep_leg(gdn, stream, with_o):
         q, k, v, g, beta, cu = (inp[x] for x in ("q", "k", "v", "g", "beta", "cu_seqlens"))
         L = int(w.lengths[0])
         S_full, _ = gdn.gdn_prefill(q, k, v, g, beta, cu, o_out=None, stream=stream)
-        t_full = _time(lambda: gdn.gdn_prefill(q, k, v, g, beta, cu, S_out=S_full, o_out=None,
-                                               stream=stream), stream, 2)
+        t_full = _time_cold(lambda: gdn.gdn_prefill(q, k, v, g, beta, cu, S_out=S_full, o_out=None,
+                                                    stream=stream), stream, 2, flush)
         rows = []
         for rho in W.GATE_SWEEP:
             rr = W.replay_len(L, rho)
@@ -329,7 +371,7 @@ def gate_sweep_leg(gdn, stream, with_o):
             o = torch.empty((rr, w.h_v, w.d_v), dtype=q.dtype, device=q.device) if with_o else None
             fn = lambda: gdn.gdn_replay(q, k, v, g, beta, cu, r, total_out_tokens=rr, S_out=S,
                                         o_out=o, stream=stream)
-            t = _time(fn, stream, 5)
+            t = _time_cold(fn, stream, 5, flush)
             rel, _ = gdn.gdn_state_relerr(S, S_full, stream=stream)
             torch.cuda.synchronize()
             rows.append({"budget": rho, "r": rr, "replay_us": t * 1e3,

@@ -685,12 +685,12 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         int64_t b = blockIdx.x;
         if (b < a.n_full) {
             if ((a.n_full & 7) == 0) b = (b & 7) * (a.n_full >> 3) + (b >> 3);
-            unit = a.unit0 + b;
+            unit = b;
         } else {
             const int64_t m = nblk - a.n_full;
             b -= a.n_full;
             if ((m & 7) == 0) b = (b & 7) * (m >> 3) + (b >> 3);
-            unit = a.unit0 + a.n_full + (b >> a.split);
+            unit = a.n_full + (b >> a.split);
             slice = (int)(b & ((1 << a.split) - 1));
             ncols = W >> a.split;
         }
@@ -1289,31 +1289,20 @@ hipError_t launch_t(const ChunkArgs &a0, hipStream_t stream)
             a.split = sp;
         }
     }
-    a.unit0 = 0;
     const int64_t nblk = a.n_full + ((units - a.n_full) << a.split);
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    // slices in which at least three state waves have no columns go to a second launch
-    // whose idle state waves help with the Gram tiles
-    const bool help = a.split > 0 && W / 16 - ((W >> a.split) / 16) >= 3;
+    // when every unit is sliced and at least three state waves of a slice have no
+    // columns, the slices run the variant whose idle state waves help with the Gram
+    // tiles (a launch with whole units too keeps one dispatch: the slices' help did not
+    // change its time)
+    const bool help = a.n_full == 0 && a.split > 0 && W / 16 - ((W >> a.split) / 16) >= 3;
     if (!help) {
         hipLaunchKernelGGL((gdn_chunk_ws_kernel<DK, DV, W, P, WITH_O, false>), dim3((unsigned)nblk),
                            dim3(64 * (W / 16 + NPW)), 0, stream, a);
         return hipGetLastError();
     }
-    if (a.n_full > 0) {   // the whole units
-        ChunkArgs w = a;
-        w.split = 0;
-        hipLaunchKernelGGL((gdn_chunk_ws_kernel<DK, DV, W, P, WITH_O, false>), dim3((unsigned)a.n_full),
-                           dim3(64 * (W / 16 + NPW)), 0, stream, w);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    ChunkArgs sl = a;     // the slices
-    sl.unit0 = a.n_full;
-    sl.n_full = 0;
-    hipLaunchKernelGGL((gdn_chunk_ws_kernel<DK, DV, W, P, WITH_O, true>),
-                       dim3((unsigned)((units - a.n_full) << a.split)), dim3(64 * (W / 16 + NPW)), 0, stream,
-                       sl);
+    hipLaunchKernelGGL((gdn_chunk_ws_kernel<DK, DV, W, P, WITH_O, true>), dim3((unsigned)nblk),
+                       dim3(64 * (W / 16 + NPW)), 0, stream, a);
     return hipGetLastError();
 }
 

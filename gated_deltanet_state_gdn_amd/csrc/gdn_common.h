@@ -24,9 +24,8 @@ struct ChunkArgs {
     int32_t o_f32;              // o stored as fp32 (1) or in the input dtype (0)
     float scale;
     // grid plan (set by the launcher): blocks [0, n_full) take whole work units, the
-    // rest take 1/2^split of a unit's columns each, starting at work unit unit0
+    // rest take 1/2^split of a unit's columns each
     int64_t n_full;
-    int64_t unit0;
     int32_t split;
 };
 
