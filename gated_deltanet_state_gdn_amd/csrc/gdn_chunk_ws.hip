@@ -973,10 +973,19 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, OT[tt]), rs,
                                                                    ob + (uint32_t)(16 * tt) * orow, 0, 0);
                     } else {
+                        // two token tiles per store: swapping lane rows 1, 3 of tile ta with rows
+                        // 0, 2 of tile tb gives every lane 8 consecutive columns (16 bytes) of one
+                        // token -- rows 0, 2 token 16 ta + l%16, rows 1, 3 token 16 tb + l%16
 #pragma unroll
-                        for (int tt = 0; tt < 4; ++tt) {
-                            const u32x2 pk = {pk_bf16(OT[tt][0], OT[tt][1]), pk_bf16(OT[tt][2], OT[tt][3])};
-                            __builtin_amdgcn_raw_buffer_store_b64(pk, rs, ob + (uint32_t)(16 * tt) * orow, 0, 0);
+                        for (int tp = 0; tp < 2; ++tp) {
+                            const int ta = 2 * tp, tb = 2 * tp + 1;
+                            const auto s0 = __builtin_amdgcn_permlane16_swap(pk_bf16(OT[ta][0], OT[ta][1]),
+                                                                             pk_bf16(OT[tb][0], OT[tb][1]), false, false);
+                            const auto s1 = __builtin_amdgcn_permlane16_swap(pk_bf16(OT[ta][2], OT[ta][3]),
+                                                                             pk_bf16(OT[tb][2], OT[tb][3]), false, false);
+                            const u32x4 w = {s0[0], s1[0], s0[1], s1[1]};
+                            const uint32_t tok = (uint32_t)(16 * ((lg & 1) ? tb : ta) + lr);
+                            __builtin_amdgcn_raw_buffer_store_b128(w, rs, tok * orow + (uint32_t)(16 * (lg >> 1)), 0, 0);
                         }
                     }
                 }
