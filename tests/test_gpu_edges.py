@@ -291,3 +291,32 @@ def test_bf16_large_values_inside_the_fp16_operand_range(mu):
         say("  mu %.0f %s: max|S| %.1f  relerr S %.3e  o %.3e" % (mu, mode, float(np.abs(S_ref).max()), eS, eo))
         assert np.isfinite(eS) and np.isfinite(eo)
         assert eS <= TOL["bf16"] and eo <= TOL["bf16"], (mode, eS, eo)
+
+
+def test_bf16_range_contract_edge_and_beyond():
+    # The header's range contract for bf16 inputs: state entries below ~10^3.  At its edge
+    # (v scaled by 256, exact in bf16) the error must stay that of unit-scale values; far
+    # beyond it (v scaled by 2^16, |S| in the 10^5 range, past fp16's 65504) the results
+    # turn non-finite, and the error report's non-finite count must show it.
+    import gated_deltanet_state_gdn_amd as gdn
+    w = W.small(W.config(1), L=[1500, 700], r=[1200, 300], h_qk=2, h_v=4, g_mu=-8.0, g_sigma=0.5)
+    base = W.make_inputs(w)
+    for scale, inside in ((256.0, True), (65536.0, False)):
+        inp = dict(base)
+        inp["v"] = (base["v"].float() * scale).to(base["v"].dtype)
+        S, o, _ = gpu_run(to_dev(inp), "replay")
+        torch.cuda.synchronize()
+        S_ref, o_ref = oracle_run(inp, "replay")
+        smax = float(np.abs(S_ref).max())
+        if inside:
+            eS, eo = compare(inp, "replay", S, o, S_ref, o_ref)
+            say("  v x %.0f: max|S| %.0f  relerr S %.3e  o %.3e" % (scale, smax, eS, eo))
+            assert smax > 500.0
+            assert eS <= TOL["bf16"] and eo <= TOL["bf16"], (eS, eo)
+        else:
+            ref = torch.from_numpy(S_ref.astype(np.float32)).cuda()
+            rel, nf = gdn.gdn_state_relerr(S, ref)
+            torch.cuda.synchronize()
+            say("  v x %.0f: max|S| %.0f  non-finite entries flagged %d" % (scale, smax, int(nf.sum())))
+            assert smax > 65504.0 and int(nf.sum()) > 0
+
