@@ -70,6 +70,7 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 
 constexpr int CH = 64;       // chunk length (tokens)
+constexpr int kOrderSeqs = 256;   // most packed sequences a launch orders by length
 constexpr int NPW = 8;       // prep waves per workgroup
 
 // Two floats to a bf16 pair (round to nearest even), the first in the low half: the
@@ -137,6 +138,13 @@ template <class P>
 __device__ __forceinline__ float v_at(typename Raw<P>::T v) {
     if constexpr (P::kBF16) return __uint_as_float((uint32_t)v << 16);
     else return __uint_as_float(v);
+}
+
+// A value that is the same in every lane of the wave, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 // ---------------------------------------------------------------- LDS layouts
@@ -677,23 +685,81 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
     // unit's prep work), so that round fills more of the chip.  Within each range the
     // order is XCD-aware: consecutive logical blocks (the slices of a unit, the v-heads
     // of one q/k head, the heads of one sequence) share an XCD's L2.
+    //
+    // Packed sequences of different lengths (2 to kOrderSeqs of them) are taken longest
+    // window first: every block ranks the sequences by chunk count (ties by index) in LDS
+    // and maps its logical position through that order, so that the long chains start in
+    // the first round and the short ones fill in behind them.  Whole units then go out in
+    // groups of 16 blocks, the two v-heads of a q/k-head pair on one XCD (blocks 2x and
+    // 2x + 1 of a group to XCD x).  Equal lengths keep the interleave above.
     const int64_t nblk = (int64_t)gridDim.x;
+    const int64_t ups = (int64_t)NCB * a.h_v;      // units per sequence
     int64_t unit;
     int slice = 0;
     int ncols = W;                         // columns of this block
+    // (the ordering pass keeps every sequence's cu_seqlens pair and r in LDS, so that the
+    // window below comes from there instead of from a second round of global loads)
+    const int *lcu0 = nullptr, *lcu1 = nullptr, *lrr = nullptr;
     {
+        bool lpt = false;
+        const int *lord = nullptr;
+        if (a.n_seqs >= 2 && a.n_seqs <= kOrderSeqs) {
+            // (buffer 1's K rows are free until the first chunk is staged)
+            int *lb0 = reinterpret_cast<int *>(smem + L::BUF + L::oK);
+            int *lb1 = lb0 + kOrderSeqs, *lr = lb1 + kOrderSeqs;
+            int *lnch = lr + kOrderSeqs;
+            int *lo = lnch + kOrderSeqs;
+            int *ldiff = lo + kOrderSeqs;
+            if (tid == 0) *ldiff = 0;
+            for (int m = tid; m < a.n_seqs; m += NTHR) {
+                const int b0 = a.cu[m], b1 = a.cu[m + 1];
+                const int rr = a.r ? a.r[m] : 0;
+                lb0[m] = b0;
+                lb1[m] = b1;
+                lr[m] = rr;
+                int64_t len = a.r ? (int64_t)rr : (int64_t)b1 - b0;
+                if (b0 < 0 || b1 < b0 || b1 > a.total_tokens || len < 0 || len > (int64_t)b1 - b0) len = 0;
+                lnch[m] = (int)((len + CH - 1) / CH);
+            }
+            __syncthreads();
+            for (int m = tid; m < a.n_seqs; m += NTHR) {
+                const int km = lnch[m];
+                int rank = 0;
+                for (int j = 0; j < a.n_seqs; ++j) {
+                    const int kj = lnch[j];
+                    rank += (kj > km || (kj == km && j < m)) ? 1 : 0;
+                }
+                lo[rank] = m;
+                if (km != lnch[0]) *ldiff = 1;
+            }
+            __syncthreads();
+            lpt = *ldiff != 0;
+            lord = lo;
+            lcu0 = lb0;
+            lcu1 = lb1;
+            lrr = lr;
+        }
         int64_t b = blockIdx.x;
         if (b < a.n_full) {
-            if ((a.n_full & 7) == 0) b = (b & 7) * (a.n_full >> 3) + (b >> 3);
-            unit = b;
+            if (lpt) {
+                if (b < (a.n_full & ~(int64_t)15))
+                    b = (b & ~(int64_t)15) + 2 * (b & 7) + ((b >> 3) & 1);
+                unit = (int64_t)lord[b / ups] * ups + b % ups;
+            } else {
+                if ((a.n_full & 7) == 0) b = (b & 7) * (a.n_full >> 3) + (b >> 3);
+                unit = b;
+            }
         } else {
             const int64_t m = nblk - a.n_full;
             b -= a.n_full;
             if ((m & 7) == 0) b = (b & 7) * (m >> 3) + (b >> 3);
             unit = a.n_full + (b >> a.split);
+            if (lpt) unit = (int64_t)lord[unit / ups] * ups + unit % ups;
             slice = (int)(b & ((1 << a.split) - 1));
             ncols = W >> a.split;
         }
+        // the unit is the same in every lane: scalar registers, scalar address arithmetic
+        unit = uniform64(unit);
     }
     const int cb = (int)(unit % NCB);
     const int h = (int)((unit / NCB) % a.h_v);
@@ -721,16 +787,17 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         bad = __syncthreads_or(bad);
         if (tid == 0 && bad) atomicOr(a.status, kStatusBitInput);
     }
-    const int64_t beg = a.cu[n], end = a.cu[n + 1];
+    const int64_t beg = __builtin_amdgcn_readfirstlane(lcu0 ? lcu0[n] : a.cu[n]);
+    const int64_t end = __builtin_amdgcn_readfirstlane(lcu1 ? lcu1[n] : a.cu[n + 1]);
     if (beg < 0 || end < beg || end > a.total_tokens) return;
-    const int64_t rn = replay ? (int64_t)a.r[n] : end - beg;
+    const int64_t rn = replay ? (int64_t)__builtin_amdgcn_readfirstlane(lrr ? lrr[n] : a.r[n]) : end - beg;
     if (rn < 0 || rn > end - beg) return;
     const int64_t wbeg = end - rn;              // first token of the window
     if (wave == 0) {
         int64_t row0 = beg;
         if (replay) {
             int64_t s = 0;
-            for (int m = lane; m < n; m += 64) s += a.r[m];
+            for (int m = lane; m < n; m += 64) s += lrr ? lrr[m] : a.r[m];
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
             row0 = s;
