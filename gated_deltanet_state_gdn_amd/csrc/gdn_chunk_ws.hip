@@ -140,6 +140,15 @@ __device__ __forceinline__ float v_at(typename Raw<P>::T v) {
     else return __uint_as_float(v);
 }
 
+// The lane index, computed afresh where it is called (an opaque all-ones mask keeps the
+// compiler from hoisting it out of a loop): inside the chunk loops this costs two vector
+// instructions instead of a register held across the whole loop.
+__device__ __forceinline__ int fresh_lane() {
+    uint32_t m = ~0u;
+    asm volatile("" : "+s"(m));
+    return (int)__builtin_amdgcn_mbcnt_hi(m, __builtin_amdgcn_mbcnt_lo(m, 0u));
+}
+
 // A value that is the same in every lane of the wave, moved to scalar registers.
 __device__ __forceinline__ int64_t uniform64(int64_t v) {
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -177,6 +186,22 @@ __device__ __forceinline__ F frag_sw(const char *M, int r0, int kb, int lane) {
     return __builtin_bit_cast(
         F, *reinterpret_cast<const u32x4 *>(M + chunk_at<RB>(r0 + (lane & 15), 4 * kb + (lane >> 4))));
 }
+// The same addresses with one XOR per k-block.  The swizzle depends only on the row's
+// low four bits, which r0 (a multiple of 16) leaves alone, and the logical chunk
+// 4 kb + g is 4 kb XOR g, so
+//     chunk_at(r0 + l%16, 4 kb + l/16) = r0 RB + (fo ^ 64 kb),
+//     fo = (l%16) RB + 16 ((l/16) ^ swz(l%16)),
+// since every term stays below RB (no carries).  An offset that is a multiple of 256 (a
+// chunk buffer) may be added to fo before the XOR.
+template <int RB>
+__device__ __forceinline__ uint32_t frag_off(int lane) {
+    const int r = lane & 15;
+    return (uint32_t)(r * RB + 16 * ((lane >> 4) ^ swz<RB>(r)));
+}
+template <class F>
+__device__ __forceinline__ F frag_at(const char *p) {
+    return __builtin_bit_cast(F, *reinterpret_cast<const u32x4 *>(p));
+}
 // bf16 fragment of K^T for one 16x16x32 product, read transposed from the row-major K:
 // lane l gets K[32 kb + {4 (l/16) + i, 16 + 4 (l/16) + i}][16 rt + l%16], i = 0..3.  The
 // transposing read hands lane n of every 16-lane group column n%4 of rows
@@ -195,6 +220,27 @@ __device__ __forceinline__ h16x8 frag_kt(const char *K, int rt, int kb, int lane
     const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
     return __builtin_bit_cast(h16x8, u32x4{ua.x, ua.y, ub.x, ub.y});
 }
+// Lane part of the transposing reads' addresses (frag_kt, frag_v), by the argument of
+// frag_off: with m = l%16 and row 4 (l/16) + m/4 inside a 16-row block,
+//     chunk_at(R0 + row, 4 j + m%4) + 8 h = R0 RB + (to ^ 64 j) + 8 h,
+//     to = row RB + 16 ((m%4) ^ swz(row)),
+// for R0 a multiple of 16 (32 kb for K^T rows, 16 tt for V rows).
+template <int RB>
+__device__ __forceinline__ uint32_t tr_off(int lane) {
+    const int m = lane & 15;
+    const int row = 4 * (lane >> 4) + (m >> 2);
+    return (uint32_t)(row * RB + 16 * ((m & 3) ^ swz<RB>(row)));
+}
+// frag_kt from tr_off: K points at the K rows of a chunk buffer (tob = to + buffer offset)
+template <int RB>
+__device__ __forceinline__ h16x8 frag_kt_at(const char *K, uint32_t tob, int rt, int kb) {
+    const char *p = K + 32 * kb * RB + (tob ^ (uint32_t)(64 * (rt >> 1))) + 8 * (rt & 1);
+    typedef __attribute__((address_space(3))) i16x4 *lds_i16x4;
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)p);
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(p + 16 * RB));
+    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+    return __builtin_bit_cast(h16x8, u32x4{ua.x, ua.y, ub.x, ub.y});
+}
 // V values of one 16-row tile in the accumulator layout, from the bf16 V rows staged in the
 // same permuted, swizzled layout as K: lane l gets V[16 tt + 4 (l/16) + i][16 ct + l%16],
 // i = 0..3, as bf16 pairs (element i in half i%2 of word i/2).  One transposing read: lane
@@ -206,6 +252,12 @@ __device__ __forceinline__ u32x2 frag_v(const char *V, int ct, int tt, int lane)
     const char *p = V + chunk_at<RB>(row, 4 * (ct >> 1) + (m & 3)) + 8 * (ct & 1);
     typedef __attribute__((address_space(3))) i16x4 *lds_i16x4;
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)p));
+}
+// frag_v from vo = tr_off ^ 64 (ct/2) + 8 (ct%2) + buffer offset (V: the staged V rows)
+template <int RB>
+__device__ __forceinline__ u32x2 frag_v_at(const char *V, uint32_t vo, int tt) {
+    typedef __attribute__((address_space(3))) i16x4 *lds_i16x4;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(V + 16 * tt * RB + vo)));
 }
 // fp32 fragment of M^T (the rows of M are the contraction index): lane l gives column
 // c0 + l%16 and rows 16 kb + 4 (l/16) + i.
@@ -423,15 +475,19 @@ struct TileIn {
 // (tile_load and tile_mma cover the k-blocks [KB0, KB1) of d_k: all of them, or one half
 // at a time where a whole tile's fragments would not fit in registers)
 template <int DK, class P, bool WITH_O, class L, int KB0 = 0, int KB1 = DK / P::KB>
-__device__ __forceinline__ void tile_load(TileIn<P, DK / P::KB> &t, const char *buf, const char *Qb,
+__device__ __forceinline__ void tile_load(TileIn<P, DK / P::KB> &t, const char *buf, const char *lds, uint32_t bo,
                                           int ti, int tj, int lane) {
     typedef typename P::Frag F;
     const float *gH = reinterpret_cast<const float *>(buf + L::oGate);
+    // fragment addresses by frag_off (bo: the chunk buffer's offset in LDS)
+    const uint32_t fo = frag_off<L::RBK>(lane);
+    const uint32_t fob = fo + bo, qob = L::Q1 ? fo : fob;
+    const char *Kb = lds + L::oK, *Qb = lds + (L::Q1 ? L::oQ1 : L::oQ);
 #pragma unroll
     for (int kb = KB0; kb < KB1; ++kb) {
-        t.kj[kb] = frag_sw<L::RBK, F>(buf + L::oK, 16 * tj, kb, lane);
-        t.ki[kb] = frag_sw<L::RBK, F>(buf + L::oK, 16 * ti, kb, lane);
-        if constexpr (WITH_O) t.qi[kb] = frag_sw<L::RBK, F>(Qb, 16 * ti, kb, lane);
+        t.kj[kb] = frag_at<F>(Kb + 16 * tj * L::RBK + (fob ^ (64u * kb)));
+        t.ki[kb] = frag_at<F>(Kb + 16 * ti * L::RBK + (fob ^ (64u * kb)));
+        if constexpr (WITH_O) t.qi[kb] = frag_at<F>(Qb + 16 * ti * L::RBK + (qob ^ (64u * kb)));
     }
     const int rr = 16 * ti + (lane & 15);
     t.hr = gH[rr];
@@ -569,7 +625,7 @@ __device__ __forceinline__ void diag_inverse(f32x4 Nr, E *Tt, int lane) {
 // products are also kept apart from the Gram products (interleaving the two in one
 // schedule gave wrong results).
 template <int PW, int DK, class P, bool WITH_O, class L, int NT1 = 2>
-__device__ __forceinline__ void prep_tiles(char *buf, const char *Qb, int lane, float scale) {
+__device__ __forceinline__ void prep_tiles(char *buf, const char *lds, uint32_t bo, int lane, float scale) {
     typedef typename P::E E;
     constexpr int KBK = DK / P::KB;
     constexpr int NT = PW < 4 ? 1 : PW < 7 ? NT1 : 0;
@@ -584,10 +640,10 @@ __device__ __forceinline__ void prep_tiles(char *buf, const char *Qb, int lane, 
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             __builtin_amdgcn_sched_barrier(0);
-            tile_load<DK, P, WITH_O, L, 0, KBK / 2>(in, buf, Qb, TI[n], TJ[n], lane);
+            tile_load<DK, P, WITH_O, L, 0, KBK / 2>(in, buf, lds, bo, TI[n], TJ[n], lane);
             tile_mma<DK, P, WITH_O, 0, KBK / 2>(in, kk, qk);
             __builtin_amdgcn_sched_barrier(0);
-            tile_load<DK, P, WITH_O, L, KBK / 2, KBK>(in, buf, Qb, TI[n], TJ[n], lane);
+            tile_load<DK, P, WITH_O, L, KBK / 2, KBK>(in, buf, lds, bo, TI[n], TJ[n], lane);
             tile_mma<DK, P, WITH_O, KBK / 2, KBK>(in, kk, qk);
             __builtin_amdgcn_sched_barrier(0);
             const f32x4 av = tile_store<DK, P, WITH_O, L>(buf, in.hr, in.lr, in.br, in.rho, in.hc, in.lc, kk, qk,
@@ -602,7 +658,7 @@ __device__ __forceinline__ void prep_tiles(char *buf, const char *Qb, int lane, 
     } else if constexpr (NT > 0) {
         TileIn<P, KBK> in;
         f32x4 kk, qk, Nr;
-        tile_load<DK, P, WITH_O, L>(in, buf, Qb, TI[0], TJ[0], lane);
+        tile_load<DK, P, WITH_O, L>(in, buf, lds, bo, TI[0], TJ[0], lane);
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             __builtin_amdgcn_sched_barrier(0);
@@ -611,7 +667,7 @@ __device__ __forceinline__ void prep_tiles(char *buf, const char *Qb, int lane, 
             const int rho = in.rho;
             const f32x4 hc = in.hc, lc = in.lc;
             __builtin_amdgcn_sched_barrier(0);
-            if (n + 1 < NT) tile_load<DK, P, WITH_O, L>(in, buf, Qb, TI[n + 1], TJ[n + 1], lane);
+            if (n + 1 < NT) tile_load<DK, P, WITH_O, L>(in, buf, lds, bo, TI[n + 1], TJ[n + 1], lane);
             __builtin_amdgcn_sched_barrier(0);
             const f32x4 av = tile_store<DK, P, WITH_O, L>(buf, hr, lr, br, rho, hc, lc, kk, qk, TI[n], TJ[n],
                                                           lane, scale);
@@ -628,7 +684,7 @@ __device__ __forceinline__ void prep_tiles(char *buf, const char *Qb, int lane, 
 // One off-diagonal Gram tile (TI > TJ) formed by a helper wave: the second tile of prep
 // wave 4, 5 or 6 (HW = 0, 1, 2), the same arithmetic as there.
 template <int HW, int DK, class P, bool WITH_O, class L>
-__device__ __forceinline__ void help_tile(char *buf, const char *Qb, int lane, float scale) {
+__device__ __forceinline__ void help_tile(char *buf, const char *lds, uint32_t bo, int lane, float scale) {
     typedef typename P::E E;
     constexpr int KBK = DK / P::KB;
     constexpr int TI = HW == 2 ? 3 : HW + 2, TJ = HW == 2 ? 2 : 0;
@@ -636,13 +692,13 @@ __device__ __forceinline__ void help_tile(char *buf, const char *Qb, int lane, f
     TileIn<P, KBK> in;
     f32x4 kk, qk;
     if constexpr (PIPE) {
-        tile_load<DK, P, WITH_O, L>(in, buf, Qb, TI, TJ, lane);
+        tile_load<DK, P, WITH_O, L>(in, buf, lds, bo, TI, TJ, lane);
         tile_mma<DK, P, WITH_O>(in, kk, qk);
     } else {
-        tile_load<DK, P, WITH_O, L, 0, KBK / 2>(in, buf, Qb, TI, TJ, lane);
+        tile_load<DK, P, WITH_O, L, 0, KBK / 2>(in, buf, lds, bo, TI, TJ, lane);
         tile_mma<DK, P, WITH_O, 0, KBK / 2>(in, kk, qk);
         __builtin_amdgcn_sched_barrier(0);
-        tile_load<DK, P, WITH_O, L, KBK / 2, KBK>(in, buf, Qb, TI, TJ, lane);
+        tile_load<DK, P, WITH_O, L, KBK / 2, KBK>(in, buf, lds, bo, TI, TJ, lane);
         tile_mma<DK, P, WITH_O, KBK / 2, KBK>(in, kk, qk);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -666,6 +722,8 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
     constexpr int NCB = DV / W;            // column blocks per head
     constexpr int RBK = L::RBK;
     static_assert(L::bytes <= 160 * 1024, "LDS plan");
+    // a chunk buffer's offset leaves the bits that the fragment XORs touch alone
+    static_assert(L::BUF % L::RBK == 0 && L::BUF % L::RBV == 0 && L::BUF % 256 == 0, "buffer alignment");
 
     __shared__ __attribute__((aligned(16))) char smem[L::bytes];
     int64_t *gMisc = reinterpret_cast<int64_t *>(smem + L::oMisc);
@@ -761,12 +819,13 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         // the unit is the same in every lane: scalar registers, scalar address arithmetic
         unit = uniform64(unit);
     }
-    const int cb = (int)(unit % NCB);
-    const int h = (int)((unit / NCB) % a.h_v);
-    const int n = (int)(unit / ((int64_t)NCB * a.h_v));
+    // (the 64-bit divisions expand to vector code: their results go back to scalar registers)
+    const int cb = __builtin_amdgcn_readfirstlane((int)(unit % NCB));
+    const int h = __builtin_amdgcn_readfirstlane((int)((unit / NCB) % a.h_v));
+    const int n = __builtin_amdgcn_readfirstlane((int)(unit / ((int64_t)NCB * a.h_v)));
     const int c_lo = cb * W + slice * ncols;            // first d_v column of the block
     const int nact = ncols / 16;                        // state waves with columns
-    const int hk = (int)(((int64_t)h * a.h_qk) / a.h_v);
+    const int hk = __builtin_amdgcn_readfirstlane((int)(((int64_t)h * a.h_qk) / a.h_v));
     const bool replay = a.r != nullptr;
 
     // ---- window selection (validates the device-resident cu_seqlens / r)
@@ -828,7 +887,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
     const E *qg = reinterpret_cast<const E *>(a.q);
     const E *kg = reinterpret_cast<const E *>(a.k);
     const E *vg = reinterpret_cast<const E *>(a.v);
-    const int64_t sbase = ((int64_t)n * a.h_v + h) * DK * DV;
+    const int64_t sbase = uniform64(((int64_t)n * a.h_v + h) * DK * DV);
 
     // HELP: three state waves without columns form the second Gram tiles of prep waves
     // 4..6, which shortens the prep waves' chain (it sets the chunk period when only a few
@@ -838,16 +897,15 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         if (HELP && hw < 3) {
             int htarget = 0;
             auto help = [&](int64_t cc) {
-                int lane = lane0;
-                asm volatile("" : "+v"(lane));
+                const int lane = fresh_lane();
                 htarget += NPW;                     // after the prep waves' staging of chunk cc
                 lds_wait_ge(pctr, htarget, pfail);
-                char *buf = smem + (cc & 1) * L::BUF;
-                const char *Qb = L::q_rows(smem, buf);
+                const uint32_t bo = (uint32_t)((cc & 1) * L::BUF);
+                char *buf = smem + bo;
                 switch (hw) {
-                case 0: help_tile<0, DK, P, WITH_O, L>(buf, Qb, lane, a.scale); break;
-                case 1: help_tile<1, DK, P, WITH_O, L>(buf, Qb, lane, a.scale); break;
-                default: help_tile<2, DK, P, WITH_O, L>(buf, Qb, lane, a.scale); break;
+                case 0: help_tile<0, DK, P, WITH_O, L>(buf, smem, bo, lane, a.scale); break;
+                case 1: help_tile<1, DK, P, WITH_O, L>(buf, smem, bo, lane, a.scale); break;
+                default: help_tile<2, DK, P, WITH_O, L>(buf, smem, bo, lane, a.scale); break;
                 }
             };
             if (nch > 0) help(0);
@@ -883,8 +941,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         const uint32_t vrow = (uint32_t)a.h_v * (uint32_t)(DV * sizeof(E));   // bytes per token
         typename Raw<P>::T vreg[4][4];
         auto fetch_v = [&](int64_t cc) {
-            int lane = lane0;
-            asm volatile("" : "+v"(lane));
+            const int lane = fresh_lane();
             const int64_t ln = (rn - cc) < CH ? (rn - cc) : CH;
             const Rsrc rs = make_rsrc(vg + ((wbeg + cc) * a.h_v + h) * (int64_t)DV + col0,
                                       ln * (int64_t)vrow);
@@ -912,14 +969,18 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             const int len = (int)((rn - c0) < CH ? (rn - c0) : CH);
             // lane-derived indices are recomputed each chunk instead of being held in
             // registers across the whole loop
-            int lane = lane0;
-            asm volatile("" : "+v"(lane));
+            const int lane = fresh_lane();
             const int lr = lane & 15, lg = lane >> 4;
             const char *buf = smem + (c & 1) * L::BUF;
             const char *Ks = buf + L::oK;
             const char *Qs = L::q_rows(smem, buf);
             const float *gH = reinterpret_cast<const float *>(buf + L::oGate);
             const float *gE = gH + CH, *gB = gE + CH, *gL = gB + CH, *gEs = gL + CH;
+            // fragment address offsets, the chunk buffer's folded in (frag_off, tr_off)
+            const uint32_t bo = (uint32_t)((c & 1) * L::BUF);
+            const uint32_t fo = frag_off<RBK>(lane);
+            const uint32_t fob = fo + bo, qob = L::Q1 ? fo : fob;
+            const char *Qb = smem + (L::Q1 ? L::oQ1 : L::oQ);
 
             // X = K S and (Q S)^T = S^T Q^T, by k-block (S rounded once to the operand type)
             f32x4 X[4], OT[4];
@@ -933,11 +994,16 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                 Frag sh;
                 if constexpr (P::kBF16) sh = bfrag(S[2 * kb], S[2 * kb + 1]);
                 else sh = S[kb];
+                // this k-block's offsets formed here, not all four ahead of time
+                uint32_t fk = fob;
+                asm volatile("" : "+v"(fk));
+                fk ^= 64u * kb;
+                const uint32_t qk = L::Q1 ? (qob ^ (64u * kb)) : fk;
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
-                    X[tt] = mma(X[tt], frag_sw<RBK, Frag>(Ks, 16 * tt, kb, lane), sh);
+                    X[tt] = mma(X[tt], frag_at<Frag>(smem + L::oK + 16 * tt * RBK + fk), sh);
                     if constexpr (WITH_O) {
-                        const Frag qf = frag_sw<RBK, Frag>(Qs, 16 * tt, kb, lane);
+                        const Frag qf = frag_at<Frag>(Qb + 16 * tt * RBK + qk);
                         OT[tt] = mma(OT[tt], sh, qf);
                     }
                 }
@@ -947,13 +1013,15 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                 if (lane == 0) __hip_atomic_fetch_add(qctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
             // Y = b (V - e X), in place
+            const uint32_t vo = P::kBF16 ? ((tr_off<L::RBV>(lane) + bo) ^ (uint32_t)(64 * (vct >> 1))) + 8u * (vct & 1)
+                                         : 0u;
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 const f32x4 br = *reinterpret_cast<const f32x4 *>(gB + 16 * tt + 4 * lg);
                 const f32x4 er = *reinterpret_cast<const f32x4 *>(gE + 16 * tt + 4 * lg);
                 f32x4 vv;
                 if constexpr (P::kBF16) {
-                    const u32x2 w = frag_v<L::RBV>(buf + L::oV, vct, tt, lane);
+                    const u32x2 w = frag_v_at<L::RBV>(smem + L::oV, vo, tt);
                     vv = f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
                                 __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
                 } else {
@@ -1068,6 +1136,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                     for (int rt = 0; rt < RT; ++rt) S[rt] *= rn;
                 }
                 Frag dh[KBT];
+                const uint32_t tob = tr_off<RBK>(lane) + bo;
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
                     const f32x4 l4 = *reinterpret_cast<const f32x4 *>(gL + 16 * tt + 4 * lg);
@@ -1085,7 +1154,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
 #pragma unroll
                     for (int kb = 0; kb < KBT; ++kb) {
                         if constexpr (P::kBF16) {
-                            s = mma(s, frag_kt<RBK>(Ks, rt, kb, lane), dh[kb]);
+                            s = mma(s, frag_kt_at<RBK>(smem + L::oK, tob, rt, kb), dh[kb]);
                         } else {
                             s = mma(s, frag_cols_f32<RBK>(Ks, 16 * rt, kb, lane), dh[kb]);
                         }
@@ -1101,8 +1170,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         const float sig = nch > 0 ? reinterpret_cast<const float *>(smem + ((nch - 1) & 1) * L::BUF +
                                                                     L::oGate)[6 * CH + 1]
                                   : 1.f;
-        int wl = lane0;
-        asm volatile("" : "+v"(wl));
+        const int wl = fresh_lane();
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -1135,7 +1203,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         // lanes of the upper half of a row write them in the other order, so that each
         // store's eight lanes of one row hit eight distinct 16-byte slots modulo 128 bytes,
         // the stores' bank rule)
-        const int spt = 64 * pw + lane0;
+        const int spt = 64 * pw + fresh_lane();
         const bool s_act = UT >= TH || spt < UT;   // with fewer units than threads, the last waves idle
         const int spu = spt % NPU, srow = spt / NPU;
         // V rows (bf16 inputs): the same kind of units over the block's columns, rounded out
@@ -1171,8 +1239,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         // the chunk starting at token cc of the window into registers (rows past the
         // window read as 0: g = b = 0 there; a chunk past the window reads nothing)
         auto fetch = [&](int64_t cc) {
-            int lane = lane0;
-            asm volatile("" : "+v"(lane));
+            const int lane = fresh_lane();
             const int64_t ln = (rn - cc) < CH ? (rn - cc) : CH;
             const int64_t t0 = wbeg + cc;
             if (pw == GW) {   // first, so that waiting for them waits for nothing else
@@ -1209,15 +1276,15 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         //   step 2: after the prep waves' barrier, each wave's Gram tiles and diagonal
         //           inverse; the gate scan of chunk cc + 1 (wave GW)
         auto prep = [&](int64_t cc) {
-            int lane = lane0;
-            asm volatile("" : "+v"(lane));
+            const int lane = fresh_lane();
             // step 1 is what every prep wave's barrier, and through it the state waves,
             // waits for: with all eight state waves busy it issues ahead of their work on the
             // same SIMD (measured: 6 % off the 36-layer replay; raising the Gram tiles as well
             // gains less); a column-slice block, with one or a few state waves, gains nothing
             // from it and loses up to 7 %, so it keeps the default priority
             if (nact == NSW) __builtin_amdgcn_s_setprio(3);
-            char *buf = smem + (cc & 1) * L::BUF;
+            const uint32_t bo = (uint32_t)((cc & 1) * L::BUF);
+            char *buf = smem + bo;
             char *Ks = buf + L::oK;
             char *Qs = const_cast<char *>(L::q_rows(smem, buf));
             if (s_act) {
@@ -1298,13 +1365,13 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             prep_sync(pctr, target, lane, pfail);
 
             switch (pw) {
-            case 0: prep_tiles<0, DK, P, WITH_O, L>(buf, Qs, lane, a.scale); break;
-            case 1: prep_tiles<1, DK, P, WITH_O, L>(buf, Qs, lane, a.scale); break;
-            case 2: prep_tiles<2, DK, P, WITH_O, L>(buf, Qs, lane, a.scale); break;
-            case 3: prep_tiles<3, DK, P, WITH_O, L>(buf, Qs, lane, a.scale); break;
-            case 4: prep_tiles<4, DK, P, WITH_O, L, HELP ? 1 : 2>(buf, Qs, lane, a.scale); break;
-            case 5: prep_tiles<5, DK, P, WITH_O, L, HELP ? 1 : 2>(buf, Qs, lane, a.scale); break;
-            case 6: prep_tiles<6, DK, P, WITH_O, L, HELP ? 1 : 2>(buf, Qs, lane, a.scale); break;
+            case 0: prep_tiles<0, DK, P, WITH_O, L>(buf, smem, bo, lane, a.scale); break;
+            case 1: prep_tiles<1, DK, P, WITH_O, L>(buf, smem, bo, lane, a.scale); break;
+            case 2: prep_tiles<2, DK, P, WITH_O, L>(buf, smem, bo, lane, a.scale); break;
+            case 3: prep_tiles<3, DK, P, WITH_O, L>(buf, smem, bo, lane, a.scale); break;
+            case 4: prep_tiles<4, DK, P, WITH_O, L, HELP ? 1 : 2>(buf, smem, bo, lane, a.scale); break;
+            case 5: prep_tiles<5, DK, P, WITH_O, L, HELP ? 1 : 2>(buf, smem, bo, lane, a.scale); break;
+            case 6: prep_tiles<6, DK, P, WITH_O, L, HELP ? 1 : 2>(buf, smem, bo, lane, a.scale); break;
             default: break;
             }
             if (pw == GW) gt = gate_scan<!P::kBF16>(__uint_as_float(gpf), __uint_as_float(bpf), lane);
