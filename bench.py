@@ -194,6 +194,11 @@ def main():
                                         total_out_tokens=int(inp["r_host"][0]), S_out=S1, o_out=o1,
                                         ws=ws, scale=w.scale, stream=stream)
             out["single_layer_call_us"] = _time_cold(f1, stream, 10, flush) * 1e3
+            out["single_layer_segmented"] = segmented_leg(
+                gdn, w, (q[sl], k[sl], v[sl], g[sl], beta[sl], cu1, r1), int(inp["r_host"][0]), 1, dev,
+                stream, flush)
+        elif n_seqs == 1 and w.d_k == w.d_v:
+            out["segmented"] = segmented_leg(gdn, w, (q, k, v, g, beta, cu, r), tot, 1, dev, stream, flush)
         # full prefill of the same packed prefixes (the baseline the replay replaces)
         Sp = torch.empty_like(S)
         op = torch.empty((int(q.shape[0]), w.h_v, w.d_v), dtype=q.dtype, device=dev) if with_o else None
@@ -240,6 +245,34 @@ class MallFlush:
     def __call__(self):
         self.k += 1
         self.buf.fill_(self.k)
+
+
+def segmented_leg(gdn, w, args, tot, n_seqs, dev, stream, flush, n_segments=0):
+    """One layer's replay cut into segments (gdn_replay_segmented) against the plain call,
+    cold (MALL flushed before each call): with outputs and state only, and the relative
+    error of the segmented state against the plain one."""
+    import torch
+    desc = gdn.make_desc(args[0], args[2], n_seqs, tot, w.scale)
+    ws = torch.zeros(gdn.gdn_segmented_workspace_bytes(desc, n_segments), dtype=torch.uint8, device=dev)
+    ws0 = gdn.workspace(desc, dev)
+    S0 = torch.empty((n_seqs, w.h_v, w.d_k, w.d_v), dtype=torch.float32, device=dev)
+    S1 = torch.empty_like(S0)
+    o = torch.empty((tot, w.h_v, w.d_v), dtype=args[0].dtype, device=dev)
+    # (0: the library's choice, clamp(128 / (n_seqs h_v), 1, 16) segments)
+    res = {"n_segments": n_segments if n_segments else max(1, min(16, 128 // (n_seqs * w.h_v)))}
+    for name, oo in (("with_o_us", o), ("state_only_us", None)):
+        fp = lambda: gdn.gdn_replay(*args, total_out_tokens=tot, S_out=S0, o_out=oo, ws=ws0, scale=w.scale,
+                                    stream=stream)
+        fs = lambda: gdn.gdn_replay_segmented(*args, total_out_tokens=tot, n_segments=n_segments, S_out=S1,
+                                              o_out=oo, ws=ws, scale=w.scale, stream=stream)
+        res[name] = _time_cold(fs, stream, 10, flush) * 1e3
+        res["plain_" + name] = _time_cold(fp, stream, 10, flush) * 1e3
+    rel, _ = gdn.gdn_state_relerr(S1, S0, stream=stream)
+    torch.cuda.synchronize()
+    res["relerr_S_vs_plain"] = float(rel.max())
+    if gdn.gdn_device_status(ws, stream) != 0:
+        raise RuntimeError("segmented replay: device status")
+    return res
 
 
 def _time_cold(fn, stream, reps, flush):

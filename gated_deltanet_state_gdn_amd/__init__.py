@@ -20,6 +20,7 @@ from ._lib import (GDN_BF16, GDN_F32, GdnDesc, GdnError, GDN_ERR_DEVICE_INPUT, G
                    LIB_PATH, load)
 
 __all__ = ["gdn_replay", "gdn_prefill", "gdn_state_relerr", "gdn_device_status",
+           "gdn_replay_segmented", "gdn_segmented_workspace_bytes",
            "gdn_adaptive_replay_len", "gdn_adaptive_replay_len_static",
            "gdn_workspace_bytes", "gdn_replay_len", "gdn_status_str", "gdn_abi_version",
            "GdnError", "make_desc", "workspace", "LIB_PATH", "load"]
@@ -101,6 +102,40 @@ def gdn_replay(q, k, v, g, beta, cu_seqlens, r, *, total_out_tokens: int, S_out=
                           _ptr(cu_seqlens), _ptr(r), _ptr(S_out), _ptr(o_out), _ptr(cu_out),
                           _ptr(ws), ws.numel(), _stream(stream))
     _check(code, "gdn_replay")
+    return S_out, o_out, cu_out
+
+
+def gdn_segmented_workspace_bytes(desc: GdnDesc, n_segments: int = 0) -> int:
+    return int(load().gdn_segmented_workspace_bytes(ctypes.byref(desc), int(n_segments)))
+
+
+def gdn_replay_segmented(q, k, v, g, beta, cu_seqlens, r, *, total_out_tokens: int,
+                         n_segments: int = 0, S_out=None, o_out=True, cu_out=None, ws=None,
+                         scale: float = 1.0, o_dtype=None, stream=None):
+    """Segment-parallel tail replay (see include/gdn.h); arguments as gdn_replay plus
+    ``n_segments`` (0 = the library's choice).  ``ws``, when given, must hold
+    gdn_segmented_workspace_bytes(desc, n_segments) bytes, zero-filled before first use.
+
+    Returns (S_out, o_out or None, cu_out or None).
+    """
+    lib = load()
+    n = int(cu_seqlens.shape[0]) - 1
+    desc = make_desc(q, v, n, total_out_tokens, scale, o_dtype)
+    dev = q.device
+    if S_out is None:
+        S_out = torch.empty((n, desc.h_v, desc.d_k, desc.d_v), dtype=torch.float32, device=dev)
+    if o_out is True:
+        odt = o_dtype if o_dtype is not None else q.dtype
+        o_out = torch.empty((int(total_out_tokens), desc.h_v, desc.d_v), dtype=odt, device=dev)
+    elif o_out is False:
+        o_out = None
+    if ws is None:
+        nb = gdn_segmented_workspace_bytes(desc, n_segments)
+        ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device=dev)
+    code = lib.gdn_replay_segmented(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(cu_seqlens), _ptr(r), _ptr(S_out), _ptr(o_out), _ptr(cu_out),
+                                    int(n_segments), _ptr(ws), ws.numel(), _stream(stream))
+    _check(code, "gdn_replay_segmented")
     return S_out, o_out, cu_out
 
 

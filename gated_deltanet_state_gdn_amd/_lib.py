@@ -12,12 +12,13 @@ GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_UNSUPPORTED = 0, 1, 
 GDN_ERR_ALIGN, GDN_ERR_WORKSPACE, GDN_ERR_LAUNCH, GDN_ERR_DEVICE_INPUT, GDN_ERR_HIP = 5, 6, 7, 8, 9
 GDN_ERR_DEVICE_WAIT, GDN_ERR_SCRATCH = 10, 11
 GDN_F32, GDN_BF16 = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 # every symbol include/gdn.h declares
 EXPORTS = ("gdn_abi_version", "gdn_status_str", "gdn_replay_len", "gdn_workspace_bytes",
            "gdn_replay", "gdn_prefill", "gdn_state_relerr", "gdn_device_status",
-           "gdn_adaptive_replay_len", "gdn_adaptive_replay_len_static")
+           "gdn_adaptive_replay_len", "gdn_adaptive_replay_len_static",
+           "gdn_segmented_workspace_bytes", "gdn_replay_segmented")
 
 
 class GdnDesc(ctypes.Structure):
@@ -68,6 +69,10 @@ def load() -> ctypes.CDLL:
     lib.gdn_adaptive_replay_len.restype = i32
     lib.gdn_adaptive_replay_len_static.argtypes = [dptr, vp, vp, ctypes.c_double, i32, i32, vp, vp]
     lib.gdn_adaptive_replay_len_static.restype = i32
+    lib.gdn_segmented_workspace_bytes.argtypes = [dptr, i32]
+    lib.gdn_segmented_workspace_bytes.restype = sz
+    lib.gdn_replay_segmented.argtypes = [dptr, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.gdn_replay_segmented.restype = i32
     if lib.gdn_abi_version() != ABI_VERSION:
         raise ImportError("libgdn.so ABI version mismatch")
     _lib = lib

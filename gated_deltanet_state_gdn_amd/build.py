@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["gdn_api.hip", "gdn_chunk_ws.hip", "gdn_relerr.hip", "gdn_adaptive.hip"]
+SOURCES = ["gdn_api.hip", "gdn_chunk_ws.hip", "gdn_relerr.hip", "gdn_adaptive.hip", "gdn_segment.hip"]
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 
 

@@ -105,6 +105,33 @@ int32_t run(const gdn_desc *d, const void *q, const void *k, const void *v, cons
     return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
+// Segment-parallel replay: segments per window and the workspace plan after the status
+// word -- virtual cu_seqlens, virtual r, the map launch's states (S_local and M of every
+// segment), every segment's true start state.
+int32_t seg_count(const gdn_desc *d, int32_t n_segments)
+{
+    if (n_segments > 0) return n_segments;
+    const int64_t heads = (int64_t)d->n_seqs * d->h_v;
+    const int64_t p = heads > 0 ? 128 / heads : 1;
+    return (int32_t)(p < 1 ? 1 : p > 16 ? 16 : p);
+}
+struct SegPlan {
+    size_t vcu, vr, lm, ss, bytes;
+};
+SegPlan seg_plan(const gdn_desc *d, int32_t P)
+{
+    auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    const size_t nv = (size_t)d->n_seqs * (size_t)P;
+    const size_t st = nv * (size_t)d->h_v * (size_t)d->d_k * (size_t)d->d_k * sizeof(float);
+    SegPlan s;
+    s.vcu = kWorkspaceBytes;
+    s.vr = s.vcu + up((nv + 1) * sizeof(int32_t));
+    s.lm = s.vr + up(nv * sizeof(int32_t));
+    s.ss = s.lm + 2 * st;
+    s.bytes = nv > 0 ? s.ss + st : kWorkspaceBytes;
+    return s;
+}
+
 // per-(sequence, v-head) lengths of gdn_adaptive_replay_len, after the status word
 size_t adaptive_scratch_bytes(const gdn_desc *d)
 {
@@ -168,6 +195,86 @@ int32_t gdn_prefill(const gdn_desc *d, const void *q, const void *k, const void 
 {
     return run(d, q, k, v, g, beta, cu_seqlens, nullptr, S0, S_out, o_out, nullptr, ws, ws_bytes,
                stream);
+}
+
+size_t gdn_segmented_workspace_bytes(const gdn_desc *d, int32_t n_segments)
+{
+    if (check_desc(d, true) != GDN_OK || n_segments < 0 || n_segments > 64 || d->d_k != d->d_v) return 0;
+    return seg_plan(d, seg_count(d, n_segments)).bytes;
+}
+
+int32_t gdn_replay_segmented(const gdn_desc *d, const void *q, const void *k, const void *v,
+                             const float *g, const float *beta, const int32_t *cu, const int32_t *r,
+                             float *S_out, void *o_out, int32_t *cu_out, int32_t n_segments, void *ws,
+                             size_t ws_bytes, void *stream)
+{
+    int32_t st = check_desc(d, true);
+    if (st != GDN_OK) return st;
+    if (n_segments < 0 || n_segments > 64) {
+        debug("n_segments must be in [0, 64]");
+        return GDN_ERR_SHAPE;
+    }
+    if (d->d_k != d->d_v) {
+        debug("segmented replay needs square states (d_k == d_v)");
+        return GDN_ERR_UNSUPPORTED;
+    }
+    if (!cu || !r || !S_out || !ws) return GDN_ERR_NULL;
+    const bool any_tokens = d->total_tokens > 0;
+    if (any_tokens && (!q || !k || !v || !g || !beta)) return GDN_ERR_NULL;
+    if (o_out && d->total_out_tokens > 0 && !any_tokens) return GDN_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) ||
+        !aligned16(S_out) || !aligned16(o_out) || !aligned16(ws) || ((uintptr_t)cu & 3u) ||
+        ((uintptr_t)r & 3u) || ((uintptr_t)cu_out & 3u)) {
+        debug("pointer alignment: 16 bytes required (4 for integer arrays)");
+        return GDN_ERR_ALIGN;
+    }
+    const int32_t P = seg_count(d, n_segments);
+    if ((int64_t)d->n_seqs * P > 0x7ffffffeLL) return GDN_ERR_SHAPE;
+    const SegPlan plan = seg_plan(d, P);
+    if (ws_bytes < plan.bytes) return GDN_ERR_WORKSPACE;
+    if (d->n_seqs == 0) return GDN_OK;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char *w = reinterpret_cast<char *>(ws);
+    int32_t *status = reinterpret_cast<int32_t *>(w);
+    int32_t *vcu = reinterpret_cast<int32_t *>(w + plan.vcu);
+    int32_t *vr = reinterpret_cast<int32_t *>(w + plan.vr);
+    float *lm = reinterpret_cast<float *>(w + plan.lm);
+    float *ss = reinterpret_cast<float *>(w + plan.ss);
+    const int32_t nv = d->n_seqs * P;
+    const bool bf16 = d->qkv_dtype == GDN_BF16;
+
+    hipError_t e = gdn::launch_seg_setup(cu, r, d->n_seqs, P, d->total_tokens, vcu, vr, cu_out, status, s);
+    if (e != hipSuccess) return GDN_ERR_LAUNCH;
+
+    gdn::ChunkArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.cu = vcu; a.r = vr; a.S0 = nullptr;
+    a.S_out = lm; a.o_out = nullptr; a.cu_out = nullptr;
+    a.status = status;
+    a.total_tokens = d->total_tokens;
+    a.total_out = d->total_out_tokens;
+    a.n_seqs = nv; a.h_qk = d->h_qk; a.h_v = d->h_v;
+    a.o_f32 = (d->o_dtype == GDN_F32 && bf16) ? 1 : 0;
+    a.scale = d->scale;
+    a.mpart = 1;   // every segment's S_local and transition map M in one launch
+    e = gdn::launch_chunk_ws(a, bf16, d->d_k, d->d_v, false, s);
+    if (e == hipErrorNotSupported) return GDN_ERR_UNSUPPORTED;
+    if (e != hipSuccess) return GDN_ERR_LAUNCH;
+
+    const size_t half = (size_t)nv * (size_t)d->h_v * (size_t)d->d_k * (size_t)d->d_k;
+    e = gdn::launch_seg_combine(lm, lm + half, ss, S_out, d->n_seqs, d->h_v, d->d_k, P, s);
+    if (e != hipSuccess) return GDN_ERR_LAUNCH;
+
+    if (o_out) {   // every segment again from its true start, for the outputs
+        a.mpart = 0;
+        a.S0 = ss;
+        a.S_out = lm;   // (scratch: the final state came from the combine)
+        a.o_out = o_out;
+        e = gdn::launch_chunk_ws(a, bf16, d->d_k, d->d_v, true, s);
+        if (e != hipSuccess) return GDN_ERR_LAUNCH;
+    }
+    return GDN_OK;
 }
 
 int32_t gdn_state_relerr(const float *S_a, const float *S_ref, int64_t n_states, int32_t d_k,

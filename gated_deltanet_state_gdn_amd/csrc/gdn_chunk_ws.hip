@@ -708,7 +708,12 @@ __device__ __forceinline__ void help_tile(char *buf, const char *lds, uint32_t b
 // ---------------------------------------------------------------- kernel
 // HELP: every block is a column slice in which at least three state waves have no columns
 // (the launcher guarantees it); those form three of the Gram tiles (help_tile).
-template <int DK, int DV, int W, class P, bool WITH_O, bool HELP>
+// MP: every sequence has 2 h_v head units: the first h_v the usual ones, the second h_v
+// the same chains with V taken as zero and S started from the identity (d_k = d_v), so
+// that their final S is the window's transition map M (S_end = M S_start + S_local);
+// their states follow the first n_seqs h_v ones in S_out, stored as 16 x 16 tiles (tile
+// (i, j) of a map at 256 (i d/16 + j) floats, row-major inside) for the combine's loads.
+template <int DK, int DV, int W, class P, bool WITH_O, bool HELP, bool MP = false>
 __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(ChunkArgs a)
 {
     constexpr int NSW = W / 16;            // state waves: one 16-column tile of S each
@@ -722,6 +727,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
     constexpr int NCB = DV / W;            // column blocks per head
     constexpr int RBK = L::RBK;
     static_assert(L::bytes <= 160 * 1024, "LDS plan");
+    static_assert(!MP || (DK == DV && !WITH_O), "transition maps: square states, no outputs");
     // a chunk buffer's offset leaves the bits that the fragment XORs touch alone
     static_assert(L::BUF % L::RBK == 0 && L::BUF % L::RBV == 0 && L::BUF % 256 == 0, "buffer alignment");
 
@@ -751,7 +757,8 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
     // groups of 16 blocks, the two v-heads of a q/k-head pair on one XCD (blocks 2x and
     // 2x + 1 of a group to XCD x).  Equal lengths keep the interleave above.
     const int64_t nblk = (int64_t)gridDim.x;
-    const int64_t ups = (int64_t)NCB * a.h_v;      // units per sequence
+    const int hvu = MP ? 2 * a.h_v : a.h_v;        // head units per sequence
+    const int64_t ups = (int64_t)NCB * hvu;        // units per sequence
     int64_t unit;
     int slice = 0;
     int ncols = W;                         // columns of this block
@@ -821,8 +828,10 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
     }
     // (the 64-bit divisions expand to vector code: their results go back to scalar registers)
     const int cb = __builtin_amdgcn_readfirstlane((int)(unit % NCB));
-    const int h = __builtin_amdgcn_readfirstlane((int)((unit / NCB) % a.h_v));
-    const int n = __builtin_amdgcn_readfirstlane((int)(unit / ((int64_t)NCB * a.h_v)));
+    const int hh = __builtin_amdgcn_readfirstlane((int)((unit / NCB) % hvu));
+    const int n = __builtin_amdgcn_readfirstlane((int)(unit / ups));
+    const bool mp = MP && hh >= a.h_v;                  // a transition-map unit
+    const int h = mp ? hh - a.h_v : hh;
     const int c_lo = cb * W + slice * ncols;            // first d_v column of the block
     const int nact = ncols / 16;                        // state waves with columns
     const int hk = __builtin_amdgcn_readfirstlane((int)(((int64_t)h * a.h_qk) / a.h_v));
@@ -878,7 +887,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
     const int64_t orow0 = gMisc[0];
     // output rows (and cu_out) must fit; without outputs only cu_out uses them
     if (orow0 < 0 || orow0 + rn > ((replay && WITH_O) ? a.total_out : a.total_tokens)) return;
-    if (a.cu_out && h == 0 && c_lo == 0 && tid == 0) {
+    if (a.cu_out && !mp && h == 0 && c_lo == 0 && tid == 0) {
         a.cu_out[n] = (int32_t)orow0;
         if (n == a.n_seqs - 1) a.cu_out[n + 1] = (int32_t)(orow0 + rn);
     }
@@ -887,7 +896,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
     const E *qg = reinterpret_cast<const E *>(a.q);
     const E *kg = reinterpret_cast<const E *>(a.k);
     const E *vg = reinterpret_cast<const E *>(a.v);
-    const int64_t sbase = uniform64(((int64_t)n * a.h_v + h) * DK * DV);
+    const int64_t sbase = uniform64((((int64_t)(mp ? a.n_seqs : 0) + n) * a.h_v + h) * DK * DV);
 
     // HELP: three state waves without columns form the second Gram tiles of prep waves
     // 4..6, which shortens the prep waves' chain (it sets the chunk period when only a few
@@ -926,7 +935,10 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         f32x4 S[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            if (!replay && a.S0) {
+            if (mp) {                                // a transition map starts at the identity
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[rt][i] = (16 * rt + 4 * lg + i == col0 + lr) ? 1.f : 0.f;
+            } else if (a.S0) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     S[rt][i] = a.S0[sbase + (int64_t)(16 * rt + 4 * lg + i) * DV + col0 + lr];
@@ -943,8 +955,9 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         auto fetch_v = [&](int64_t cc) {
             const int lane = fresh_lane();
             const int64_t ln = (rn - cc) < CH ? (rn - cc) : CH;
+            // (a transition map reads V as zero: an empty buffer, every load returns 0)
             const Rsrc rs = make_rsrc(vg + ((wbeg + cc) * a.h_v + h) * (int64_t)DV + col0,
-                                      ln * (int64_t)vrow);
+                                      mp ? 0 : ln * (int64_t)vrow);
             // token rows 16 tt + 4 (lane/16) + i: one running offset, one add per load
             uint32_t vo = (uint32_t)(4 * (lane >> 4)) * vrow + (uint32_t)(lane & 15) * (uint32_t)sizeof(E);
 #pragma unroll
@@ -1171,11 +1184,20 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
                                                                     L::oGate)[6 * CH + 1]
                                   : 1.f;
         const int wl = fresh_lane();
+        if (mp) {   // a transition map: 16 x 16 tiles, each 1 KB contiguous and row-major inside
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a.S_out[sbase + (int64_t)(16 * rt + 4 * (wl >> 4) + i) * DV + col0 + (wl & 15)] = S[rt][i] * sig;
+                for (int i = 0; i < 4; ++i)
+                    a.S_out[sbase + (int64_t)(rt * (DV / 16) + col0 / 16) * 256 + (4 * (wl >> 4) + i) * 16 + (wl & 15)] =
+                        S[rt][i] * sig;
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    a.S_out[sbase + (int64_t)(16 * rt + 4 * (wl >> 4) + i) * DV + col0 + (wl & 15)] = S[rt][i] * sig;
+        }
     } else {
         // =====================================================================
         // prep waves: chunk c + 1's operands while the state waves process chunk c
@@ -1263,7 +1285,9 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
             }
             if constexpr (STAGE_V) {
                 if (v_act) {
-                    const Rsrc rv = make_rsrc(vg + ((t0 * a.h_v + h) * (int64_t)DV + cb * W), ln * (int64_t)vrowp);
+                    // (a transition map stages V = 0: an empty buffer, every load returns 0)
+                    const Rsrc rv = make_rsrc(vg + ((t0 * a.h_v + h) * (int64_t)DV + cb * W),
+                                              mp ? 0 : ln * (int64_t)vrowp);
                     vpf[0] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_vo, 0, 0);
                     vpf[1] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_vo + 32u, 0, 0);
                 }
@@ -1412,10 +1436,10 @@ int64_t resident_slots()
     return v;
 }
 
-template <int DK, int DV, int W, class P, bool WITH_O>
+template <int DK, int DV, int W, class P, bool WITH_O, bool MP = false>
 hipError_t launch_t(const ChunkArgs &a0, hipStream_t stream)
 {
-    const int64_t units = (int64_t)a0.n_seqs * a0.h_v * (DV / W);
+    const int64_t units = (int64_t)a0.n_seqs * a0.h_v * (MP ? 2 : 1) * (DV / W);
     if (units <= 0) return hipSuccess;
     // split the units of a partial last round into column slices (2^split each, at least
     // 16 columns) while they still fit in one round
@@ -1440,11 +1464,11 @@ hipError_t launch_t(const ChunkArgs &a0, hipStream_t stream)
     // change its time)
     const bool help = a.n_full == 0 && a.split > 0 && W / 16 - ((W >> a.split) / 16) >= 3;
     if (!help) {
-        hipLaunchKernelGGL((gdn_chunk_ws_kernel<DK, DV, W, P, WITH_O, false>), dim3((unsigned)nblk),
+        hipLaunchKernelGGL((gdn_chunk_ws_kernel<DK, DV, W, P, WITH_O, false, MP>), dim3((unsigned)nblk),
                            dim3(64 * (W / 16 + NPW)), 0, stream, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((gdn_chunk_ws_kernel<DK, DV, W, P, WITH_O, true>), dim3((unsigned)nblk),
+    hipLaunchKernelGGL((gdn_chunk_ws_kernel<DK, DV, W, P, WITH_O, true, MP>), dim3((unsigned)nblk),
                        dim3(64 * (W / 16 + NPW)), 0, stream, a);
     return hipGetLastError();
 }
@@ -1455,6 +1479,17 @@ hipError_t launch_chunk_ws(const ChunkArgs &a, int bf16, int d_k, int d_v, bool 
 {
 #define GDN_DISPATCH(DK, DV, W, POL)                                                   \
     return with_o ? launch_t<DK, DV, W, POL, true>(a, s) : launch_t<DK, DV, W, POL, false>(a, s)
+    if (a.mpart) {   // state and transition-map units of square states, no outputs
+        if (with_o || d_k != d_v) return hipErrorNotSupported;
+        if (bf16) {
+            if (d_k == 128) return launch_t<128, 128, 128, PolBF16, false, true>(a, s);
+            if (d_k == 64) return launch_t<64, 64, 64, PolBF16, false, true>(a, s);
+        } else {
+            if (d_k == 128) return launch_t<128, 128, 64, PolF32, false, true>(a, s);
+            if (d_k == 64) return launch_t<64, 64, 64, PolF32, false, true>(a, s);
+        }
+        return hipErrorNotSupported;
+    }
     if (bf16) {
         if (d_k == 128 && d_v == 128) GDN_DISPATCH(128, 128, 128, PolBF16);
         if (d_k == 64 && d_v == 64) GDN_DISPATCH(64, 64, 64, PolBF16);

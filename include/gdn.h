@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum {
     GDN_OK = 0,
@@ -191,6 +191,31 @@ int32_t gdn_adaptive_replay_len(const gdn_desc *desc, const float *g, const int3
 int32_t gdn_adaptive_replay_len_static(const gdn_desc *desc, const float *g,
                                        const int32_t *cu_seqlens, double eps, int32_t r_min,
                                        int32_t r_max, int32_t *r_out, void *stream);
+
+/* Segment-parallel tail replay: gdn_replay's result (up to rounding) in less time when
+ * few (sequence, v-head) chains are long, e.g. one layer of one sequence.  The recurrence
+ * is affine in the state, so over any stretch of tokens S_end = M S_start + S_local, with
+ * S_local the state the stretch builds from zero and M the product of its per-token maps
+ * alpha_t (I - beta_t k_t k_t^T) (technical summary, "Mecanismos Principais", for the
+ * recurrence; the pages replay one window per layer from a zero state).  Each window is
+ * cut into P chunk-aligned segments of ceil(ceil(r/64)/P) chunks (trailing ones may be
+ * empty); one launch forms every segment's S_local and M together, a combine chains
+ * S_start(p+1) = M_p S_start(p) + S_local(p) from S_start(0) = 0 in fp32 and writes the
+ * final state to S_out, and, when o_out is given, a second launch re-runs each segment
+ * from its true start for the outputs (layouts as gdn_replay; cu_out likewise).
+ * n_segments: P in [1, 64], or 0 for clamp(128 / (n_seqs h_v), 1, 16).  Requires d_k ==
+ * d_v (else GDN_ERR_UNSUPPORTED); n_segments outside [0, 64] -> GDN_ERR_SHAPE.  The
+ * workspace must hold gdn_segmented_workspace_bytes(desc, n_segments) bytes (its first
+ * 256 are the status word, as for every call); it also carries the segments' states,
+ * 3 n_seqs P h_v d_k^2 floats.  Errors in the device cu_seqlens / r are reported through
+ * the status word as for gdn_replay.  Compared with gdn_replay: S and o agree to the
+ * rounding of the products (fp16 operands for bf16 inputs), not bit for bit. */
+size_t gdn_segmented_workspace_bytes(const gdn_desc *desc, int32_t n_segments);
+int32_t gdn_replay_segmented(const gdn_desc *desc, const void *q, const void *k, const void *v,
+                             const float *g, const float *beta, const int32_t *cu_seqlens,
+                             const int32_t *r, float *S_out, void *o_out, int32_t *cu_out,
+                             int32_t n_segments, void *workspace, size_t workspace_bytes,
+                             void *stream);
 
 /* (host, synchronising) Wait for `stream`, read the status word of `workspace` and
  * clear it.  *status_host: GDN_OK, GDN_ERR_DEVICE_INPUT (a call since the previous

@@ -34,7 +34,7 @@ def test_header_declarations_are_exported():
 
 def test_version_status_and_replay_len():
     gdn, lib = _lib()
-    assert gdn.gdn_abi_version() == 2
+    assert gdn.gdn_abi_version() == 3
     for code in range(12):
         assert gdn.gdn_status_str(code) not in ("unknown status", "")
     for L in (0, 1, 7, 64, 100, 2048, 8192, 32768, 12345):
@@ -123,3 +123,44 @@ def test_allocation_free_adaptive_rejects_oversized_requests():
     assert lib.gdn_adaptive_replay_len_static(ctypes.byref(d), PM, P, 1e-3, 0, 100, P, None) == L.GDN_ERR_ALIGN
     d.n_seqs = 0
     assert lib.gdn_adaptive_replay_len_static(ctypes.byref(d), P, P, 1e-3, 0, 100, P, None) == L.GDN_OK
+
+
+def _seg(lib, d, n_segments=0, ws_bytes=1 << 40, o=None, r=P, cu=P, S=P, q=P, ws=P):
+    return lib.gdn_replay_segmented(ctypes.byref(d) if d is not None else None, q, P, P, P, P, cu, r, S,
+                                    o, None, n_segments, ws, ws_bytes, None)
+
+
+def test_segmented_replay_host_validation():
+    gdn, lib = _lib()
+    L = gdn._lib
+    assert _seg(lib, None) == L.GDN_ERR_NULL
+    assert _seg(lib, _desc(gdn), n_segments=-1) == L.GDN_ERR_SHAPE
+    assert _seg(lib, _desc(gdn), n_segments=65) == L.GDN_ERR_SHAPE
+    assert _seg(lib, _desc(gdn, d_v=64)) == L.GDN_ERR_UNSUPPORTED        # square states only
+    assert _seg(lib, _desc(gdn, h_v=3)) == L.GDN_ERR_SHAPE
+    assert _seg(lib, _desc(gdn), r=None) == L.GDN_ERR_NULL
+    assert _seg(lib, _desc(gdn), cu=None) == L.GDN_ERR_NULL
+    assert _seg(lib, _desc(gdn), S=None) == L.GDN_ERR_NULL
+    assert _seg(lib, _desc(gdn), ws=None) == L.GDN_ERR_NULL
+    assert _seg(lib, _desc(gdn), q=PM) == L.GDN_ERR_ALIGN
+    assert _seg(lib, _desc(gdn), o=PM) == L.GDN_ERR_ALIGN
+    d = _desc(gdn)
+    need = gdn.gdn_segmented_workspace_bytes(d, 8)
+    assert _seg(lib, d, n_segments=8, ws_bytes=need - 1) == L.GDN_ERR_WORKSPACE
+    assert _seg(lib, _desc(gdn, n_seqs=0), n_segments=8, ws_bytes=256) == L.GDN_OK
+
+
+def test_segmented_workspace_bytes():
+    gdn, lib = _lib()
+    d = _desc(gdn, n_seqs=3, h_v=4, d_k=128, d_v=128)
+    up = lambda b: (b + 255) // 256 * 256
+    for P_ in (1, 5, 8):
+        nv = 3 * P_
+        st = nv * 4 * 128 * 128 * 4
+        assert gdn.gdn_segmented_workspace_bytes(d, P_) == 256 + up(4 * (nv + 1)) + up(4 * nv) + 3 * st
+    # 0 = the library's choice: clamp(128 / (n_seqs h_v), 1, 16) segments
+    assert gdn.gdn_segmented_workspace_bytes(d, 0) == gdn.gdn_segmented_workspace_bytes(d, 10)
+    assert gdn.gdn_segmented_workspace_bytes(_desc(gdn, n_seqs=1, h_v=2, h_qk=2), 0) == \
+        gdn.gdn_segmented_workspace_bytes(_desc(gdn, n_seqs=1, h_v=2, h_qk=2), 16)
+    assert gdn.gdn_segmented_workspace_bytes(_desc(gdn, d_v=64), 4) == 0      # rejected descriptor
+    assert gdn.gdn_segmented_workspace_bytes(d, 65) == 0
