@@ -258,8 +258,9 @@ def segmented_leg(gdn, w, args, tot, n_seqs, dev, stream, flush, n_segments=0):
     S0 = torch.empty((n_seqs, w.h_v, w.d_k, w.d_v), dtype=torch.float32, device=dev)
     S1 = torch.empty_like(S0)
     o = torch.empty((tot, w.h_v, w.d_v), dtype=args[0].dtype, device=dev)
-    # (0: the library's choice, clamp(128 / (n_seqs h_v), 1, 16) segments)
-    res = {"n_segments": n_segments if n_segments else max(1, min(16, 128 // (n_seqs * w.h_v)))}
+    # (0: the library's choice from the head count and the replay length, see include/gdn.h)
+    auto = max(1, min(16, 128 // (n_seqs * w.h_v), ((tot // n_seqs + 63) // 64) // 6))
+    res = {"n_segments": n_segments if n_segments else auto}
     for name, oo in (("with_o_us", o), ("state_only_us", None)):
         fp = lambda: gdn.gdn_replay(*args, total_out_tokens=tot, S_out=S0, o_out=oo, ws=ws0, scale=w.scale,
                                     stream=stream)

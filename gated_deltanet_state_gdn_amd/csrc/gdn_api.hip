@@ -108,11 +108,19 @@ int32_t run(const gdn_desc *d, const void *q, const void *k, const void *v, cons
 // Segment-parallel replay: segments per window and the workspace plan after the status
 // word -- virtual cu_seqlens, virtual r, the map launch's states (S_local and M of every
 // segment), every segment's true start state.
+// The default: enough segments that the map launch and the output launch each fill about
+// half the chip (128 / (n_seqs h_v)), but at least ~6 chunks per segment, judged from the
+// mean replay length total_out_tokens / n_seqs when it is given (measured: shorter segments
+// cost more in the extra launches and the combine than they save).
 int32_t seg_count(const gdn_desc *d, int32_t n_segments)
 {
     if (n_segments > 0) return n_segments;
     const int64_t heads = (int64_t)d->n_seqs * d->h_v;
-    const int64_t p = heads > 0 ? 128 / heads : 1;
+    int64_t p = heads > 0 ? 128 / heads : 1;
+    if (d->total_out_tokens > 0 && d->n_seqs > 0) {
+        const int64_t chunks = (d->total_out_tokens / d->n_seqs + 63) / 64;
+        if (chunks / 6 < p) p = chunks / 6;
+    }
     return (int32_t)(p < 1 ? 1 : p > 16 ? 16 : p);
 }
 struct SegPlan {
@@ -233,6 +241,8 @@ int32_t gdn_replay_segmented(const gdn_desc *d, const void *q, const void *k, co
     const SegPlan plan = seg_plan(d, P);
     if (ws_bytes < plan.bytes) return GDN_ERR_WORKSPACE;
     if (d->n_seqs == 0) return GDN_OK;
+    if (P == 1)   // one segment is the plain replay (bit for bit): run it directly
+        return run(d, q, k, v, g, beta, cu, r, nullptr, S_out, o_out, cu_out, ws, ws_bytes, stream);
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char *w = reinterpret_cast<char *>(ws);

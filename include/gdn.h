@@ -203,8 +203,11 @@ int32_t gdn_adaptive_replay_len_static(const gdn_desc *desc, const float *g,
  * S_start(p+1) = M_p S_start(p) + S_local(p) from S_start(0) = 0 in fp32 and writes the
  * final state to S_out, and, when o_out is given, a second launch re-runs each segment
  * from its true start for the outputs (layouts as gdn_replay; cu_out likewise).
- * n_segments: P in [1, 64], or 0 for clamp(128 / (n_seqs h_v), 1, 16).  Requires d_k ==
- * d_v (else GDN_ERR_UNSUPPORTED); n_segments outside [0, 64] -> GDN_ERR_SHAPE.  The
+ * n_segments: P in [1, 64], or 0 for the library's choice, clamp(min(128 / (n_seqs h_v),
+ * chunks / 6), 1, 16) with chunks = ceil(total_out_tokens / n_seqs / 64) when
+ * total_out_tokens > 0 (segments shorter than ~6 chunks cost more than they save); P = 1
+ * runs gdn_replay itself.  Requires d_k == d_v (else GDN_ERR_UNSUPPORTED); n_segments
+ * outside [0, 64] -> GDN_ERR_SHAPE.  The
  * workspace must hold gdn_segmented_workspace_bytes(desc, n_segments) bytes (its first
  * 256 are the status word, as for every call); it also carries the segments' states,
  * 3 n_seqs P h_v d_k^2 floats.  Errors in the device cu_seqlens / r are reported through

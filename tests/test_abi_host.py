@@ -158,9 +158,16 @@ def test_segmented_workspace_bytes():
         nv = 3 * P_
         st = nv * 4 * 128 * 128 * 4
         assert gdn.gdn_segmented_workspace_bytes(d, P_) == 256 + up(4 * (nv + 1)) + up(4 * nv) + 3 * st
-    # 0 = the library's choice: clamp(128 / (n_seqs h_v), 1, 16) segments
-    assert gdn.gdn_segmented_workspace_bytes(d, 0) == gdn.gdn_segmented_workspace_bytes(d, 10)
-    assert gdn.gdn_segmented_workspace_bytes(_desc(gdn, n_seqs=1, h_v=2, h_qk=2), 0) == \
-        gdn.gdn_segmented_workspace_bytes(_desc(gdn, n_seqs=1, h_v=2, h_qk=2), 16)
+    # 0 = the library's choice: clamp(min(128 / (n_seqs h_v), chunks / 6), 1, 16) segments,
+    # chunks from the mean replay length total_out_tokens / n_seqs when it is given
+    big = dict(total_tokens=200000)
+    d0 = _desc(gdn, n_seqs=3, h_v=4, total_out_tokens=0, **big)
+    assert gdn.gdn_segmented_workspace_bytes(d0, 0) == gdn.gdn_segmented_workspace_bytes(d0, 10)
+    d1 = _desc(gdn, n_seqs=1, h_v=2, h_qk=2, total_out_tokens=0, **big)
+    assert gdn.gdn_segmented_workspace_bytes(d1, 0) == gdn.gdn_segmented_workspace_bytes(d1, 16)
+    d2 = _desc(gdn, n_seqs=1, h_v=16, h_qk=16, total_out_tokens=3277, **big)     # 52 chunks
+    assert gdn.gdn_segmented_workspace_bytes(d2, 0) == gdn.gdn_segmented_workspace_bytes(d2, 8)
+    d3 = _desc(gdn, n_seqs=1, h_v=16, h_qk=16, total_out_tokens=410, **big)      # 7 chunks
+    assert gdn.gdn_segmented_workspace_bytes(d3, 0) == gdn.gdn_segmented_workspace_bytes(d3, 1)
     assert gdn.gdn_segmented_workspace_bytes(_desc(gdn, d_v=64), 4) == 0      # rejected descriptor
     assert gdn.gdn_segmented_workspace_bytes(d, 65) == 0
