@@ -273,7 +273,7 @@ int32_t gdn_replay_segmented(const gdn_desc *d, const void *q, const void *k, co
     if (e != hipSuccess) return GDN_ERR_LAUNCH;
 
     const size_t half = (size_t)nv * (size_t)d->h_v * (size_t)d->d_k * (size_t)d->d_k;
-    e = gdn::launch_seg_combine(lm, lm + half, ss, S_out, d->n_seqs, d->h_v, d->d_k, P, s);
+    e = gdn::launch_seg_combine(lm, lm + half, ss, S_out, d->n_seqs, d->h_v, d->d_k, P, bf16, s);
     if (e != hipSuccess) return GDN_ERR_LAUNCH;
 
     if (o_out) {   // every segment again from its true start, for the outputs

@@ -66,8 +66,9 @@ hipError_t launch_seg_setup(const int32_t *cu, const int32_t *r, int32_t n_seqs,
                             int32_t *status, hipStream_t stream);
 // Combine: L, M = the map launch's states [n_seqs P, h_v, d, d] each; Sstart [n_seqs P, h_v,
 // d, d] receives every segment's true start state, S_out [n_seqs, h_v, d, d] the final one.
+// split: products on fp16 hi/lo halves (bf16 inputs) instead of fp32 ones.
 hipError_t launch_seg_combine(const float *L, const float *M, float *Sstart, float *S_out, int32_t n_seqs,
-                              int32_t h_v, int32_t d, int32_t P, hipStream_t stream);
+                              int32_t h_v, int32_t d, int32_t P, bool split, hipStream_t stream);
 
 // Bits of the device status word (workspace word 0).  Kernels only ever OR bits in
 // (atomically); gdn_device_status reads the word and clears it.

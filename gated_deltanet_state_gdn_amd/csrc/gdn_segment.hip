@@ -105,26 +105,38 @@ __global__ void __launch_bounds__(1024) seg_setup_kernel(const int32_t *cu, cons
     if (bad) atomicOr(status, kStatusBitInput);
 }
 
-// Chain the segments of one (sequence, v-head) over a 16-column slice of S, in fp32 on
-// the matrix cores (16x16x4 fp32 products: exact products, fp32 sums):
+// Chain the segments of one (sequence, v-head) over a 16-column slice of S on the matrix
+// cores, fp32 sums:
 //     S = L_0;  Sstart[v_0] = 0;  for p = 1 .. P-1:  Sstart[v_p] = S;  S = M_p S + L_p;
 //     S_out = S,
 // v_p = n P + p.  L and M are the two halves of the map launch's states, each
 // [n_seqs P, h_v, DK, DK]: L_p = S_local of segment p (row-major), M_p its transition map
 // (16 x 16 tiles, tile (i, j) at 256 (i DK/16 + j), row-major inside).
+//   SPLIT = false: 16x16x4 fp32 products (exact products), for fp32 inputs.
+//   SPLIT = true (bf16 inputs, whose state is bounded by the fp16 range contract): every
+//     operand x is split into fp16 hi = fp16(x) and lo = fp16(x - hi), and M S is formed
+//     as hi*hi + hi*lo + lo*hi on 16x16x32 fp16 products (the dropped lo*lo and the
+//     roundings leave ~2^-21 relative, against the 3e-3 tolerance of bf16 inputs): an
+//     eighth of the matrix-core cycles.  S is split once, when it is written to LDS.
 // Block: DK / 16 waves, one 16-row tile of the slice each; the M and L fragments of the
 // next two steps are in flight while the current step's products run.  S lives in LDS
-// transposed ([column][row], rows padded by 4 floats so that the 16 lanes reading one
-// k-range of the 16 columns hit distinct banks), double-buffered across the steps.
-template <int DK>
+// transposed ([column][row], rows padded so that the 16 lanes reading one k-range of
+// the 16 columns hit distinct banks), double-buffered across the steps.
+template <int DK, bool SPLIT>
 __global__ void __launch_bounds__(64 * (DK / 16)) seg_combine_kernel(const float *L, const float *M, float *Sstart,
                                                                      float *S_out, int32_t n_seqs, int32_t h_v,
                                                                      int32_t P)
 {
-    constexpr int LD = DK + 4;                 // padded row (one column of S) in LDS
-    constexpr int KB = DK / 16;                // 16-wide k-blocks
+    constexpr int LD = DK + 4;                 // padded row (one column of S) in LDS, fp32
+    constexpr int LH = DK + 8;                 // the same for the fp16 halves
+    constexpr int KB = DK / 16;                // 16-wide k-blocks (fp32 fragments)
     typedef __attribute__((ext_vector_type(4))) float f4;
+    typedef __attribute__((ext_vector_type(8))) _Float16 h8;
+    typedef __attribute__((ext_vector_type(2))) _Float16 h2;
+    typedef __attribute__((ext_vector_type(2))) float f2;
     __shared__ __attribute__((aligned(16))) float st[2][16 * LD];
+    __shared__ __attribute__((aligned(16))) _Float16 sth[SPLIT ? 2 : 1][SPLIT ? 16 * LH : 8];
+    __shared__ __attribute__((aligned(16))) _Float16 stl[SPLIT ? 2 : 1][SPLIT ? 16 * LH : 8];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
@@ -141,21 +153,44 @@ __global__ void __launch_bounds__(64 * (DK / 16)) seg_combine_kernel(const float
     const int c0 = 16 * cs, r0 = 16 * wave;
     const int64_t SS = (int64_t)DK * DK;       // floats per state
     auto state_at = [&](int p) { return ((n * P + p) * h_v + h) * SS; };
-    // this lane's part of S_new = M_p S + L_p: rows r0 + 4 (l/16) + i, column c0 + l%16;
-    // M_p fragments: row r0 + l%16, columns 16 kb + 4 (l/16) .. +3.  Two register sets
-    // keep the operands of steps p + 1 and p + 2 in flight while step p runs.
+    // this lane's part of S_new = M_p S + L_p: rows r0 + 4 (l/16) + i, column c0 + l%16.
+    // M_p fragments, row r0 + l%16: fp32, columns 16 kb + 4 (l/16) .. +3 of each 16-wide
+    // block; split, columns 32 j + 8 (l/16) .. +7 of each 32-wide block (the two halves
+    // of the same KB floats).  Two register sets keep the operands of steps p + 1 and
+    // p + 2 in flight while step p runs.
     struct Ops {
         f4 m[KB];
         f4 l;
     };
     auto load = [&](Ops &o, int p) {
         const int64_t base = state_at(p);
-        // (M is stored as 16 x 16 tiles: one contiguous 1 KB load per fragment)
+        // (M is stored as 16 x 16 tiles: contiguous loads)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-            o.m[kb] = *reinterpret_cast<const f4 *>(M + base + (int64_t)(wave * KB + kb) * 256 + 16 * lr + 4 * lg);
+        for (int kb = 0; kb < KB; ++kb) {
+            if constexpr (SPLIT) {   // 32-wide block kb/2, lane group l/16: 8 floats
+                const int t = 2 * (kb >> 1) + (lg >> 1);
+                o.m[kb] = *reinterpret_cast<const f4 *>(M + base + (int64_t)(wave * KB + t) * 256 + 16 * lr +
+                                                        8 * (lg & 1) + 4 * (kb & 1));
+            } else {
+                o.m[kb] = *reinterpret_cast<const f4 *>(M + base + (int64_t)(wave * KB + kb) * 256 + 16 * lr + 4 * lg);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) o.l[i] = L[base + (int64_t)(r0 + 4 * lg + i) * DK + c0 + lr];
+    };
+    // the new S (this lane's four entries) into buffer q: fp32, and for SPLIT its halves
+    auto put_s = [&](int q, f4 x) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[q][lr * LD + r0 + 4 * lg + i] = x[i];
+        if constexpr (SPLIT) {
+            h2 h01 = __builtin_convertvector(f2{x[0], x[1]}, h2), h23 = __builtin_convertvector(f2{x[2], x[3]}, h2);
+            const f2 b01 = __builtin_convertvector(h01, f2), b23 = __builtin_convertvector(h23, f2);
+            const h2 l01 = __builtin_convertvector(f2{x[0] - b01[0], x[1] - b01[1]}, h2);
+            const h2 l23 = __builtin_convertvector(f2{x[2] - b23[0], x[3] - b23[1]}, h2);
+            typedef __attribute__((ext_vector_type(4))) _Float16 h4;
+            *reinterpret_cast<h4 *>(&sth[q][lr * LH + r0 + 4 * lg]) = h4{h01[0], h01[1], h23[0], h23[1]};
+            *reinterpret_cast<h4 *>(&stl[q][lr * LH + r0 + 4 * lg]) = h4{l01[0], l01[1], l23[0], l23[1]};
+        }
     };
     // (the 16 columns of one row: 4 consecutive per lane group, from the transposed copy)
     auto put_rows = [&](float *dst, const float *src) {
@@ -165,30 +200,50 @@ __global__ void __launch_bounds__(64 * (DK / 16)) seg_combine_kernel(const float
         *reinterpret_cast<f4 *>(dst + (int64_t)(r0 + lr) * DK + c0 + 4 * lg) = x;
     };
     int cur = 0;
-    // one step: Sstart[v_p] = S, S = M_p S + L_p, then the operands of step p + 2 into o
+    // one step: the operands of step p + 2 into o, Sstart[v_p] = S, S = M_p S + L_p
     auto step = [&](Ops &o, int p) {
-        put_rows(Sstart + state_at(p), st[cur]);
         f4 acc = o.l;
         f4 m[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) m[kb] = o.m[kb];
-        if (p + 2 < P) load(o, p + 2);
-        // every S fragment first, then two independent product chains (even and odd
-        // k-blocks), summed at the end
-        f4 bf[KB];
+        load(o, p + 2 < P ? p + 2 : P - 1);   // (unconditional: no branch around the loads)
+        // (the start state's store after the loads: a wait for those loads then never
+        // waits for this store's write as well)
+        put_rows(Sstart + state_at(p), st[cur]);
+        if constexpr (SPLIT) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) bf[kb] = *reinterpret_cast<const f4 *>(&st[cur][lr * LD + 16 * kb + 4 * lg]);
-        f4 acc2 = {0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < KB / 2; ++j) {
+                h8 ah, al;
 #pragma unroll
-        for (int kb = 0; kb < KB; kb += 2) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(m[kb][j], bf[kb][j], acc, 0, 0, 0);
-                acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(m[kb + 1][j], bf[kb + 1][j], acc2, 0, 0, 0);
+                for (int e = 0; e < 8; ++e) {
+                    const float x = m[2 * j + (e >> 2)][e & 3];
+                    ah[e] = (_Float16)x;
+                    al[e] = (_Float16)(x - (float)ah[e]);
+                }
+                const h8 bh = *reinterpret_cast<const h8 *>(&sth[cur][lr * LH + 32 * j + 8 * lg]);
+                const h8 bl = *reinterpret_cast<const h8 *>(&stl[cur][lr * LH + 32 * j + 8 * lg]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc, 0, 0, 0);
             }
-        }
+            put_s(cur ^ 1, acc);
+        } else {
+            // every S fragment first, then two independent product chains (even and odd
+            // k-blocks), summed at the end
+            f4 bf[KB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st[cur ^ 1][lr * LD + r0 + 4 * lg + i] = acc[i] + acc2[i];
+            for (int kb = 0; kb < KB; ++kb) bf[kb] = *reinterpret_cast<const f4 *>(&st[cur][lr * LD + 16 * kb + 4 * lg]);
+            f4 acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; kb += 2) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(m[kb][j], bf[kb][j], acc, 0, 0, 0);
+                    acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(m[kb + 1][j], bf[kb + 1][j], acc2, 0, 0, 0);
+                }
+            }
+            put_s(cur ^ 1, acc + acc2);
+        }
         sync_lds();
         cur ^= 1;
     };
@@ -199,11 +254,15 @@ __global__ void __launch_bounds__(64 * (DK / 16)) seg_combine_kernel(const float
         f4 z = {0.f, 0.f, 0.f, 0.f};
         *reinterpret_cast<f4 *>(Sstart + state_at(0) + (int64_t)(r0 + lr) * DK + c0 + 4 * lg) = z;
         const int64_t base = state_at(0);
+        f4 l0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st[0][lr * LD + r0 + 4 * lg + i] = L[base + (int64_t)(r0 + 4 * lg + i) * DK + c0 + lr];
+        for (int i = 0; i < 4; ++i) l0[i] = L[base + (int64_t)(r0 + 4 * lg + i) * DK + c0 + lr];
+        put_s(0, l0);
     }
-    if (P > 1) load(A, 1);
-    if (P > 2) load(B, 2);
+    if (P > 1) {
+        load(A, 1);
+        load(B, P > 2 ? 2 : 1);
+    }
     sync_lds();
     for (int p = 1; p < P; p += 2) {
         step(A, p);
@@ -224,21 +283,25 @@ hipError_t launch_seg_setup(const int32_t *cu, const int32_t *r, int32_t n_seqs,
 }
 
 hipError_t launch_seg_combine(const float *L, const float *M, float *Sstart, float *S_out, int32_t n_seqs,
-                              int32_t h_v, int32_t d, int32_t P, hipStream_t stream)
+                              int32_t h_v, int32_t d, int32_t P, bool split, hipStream_t stream)
 {
     // (sequence, head) pairs rounded up to a multiple of 8 (the XCD grouping)
     const int64_t blocks = (((int64_t)n_seqs * h_v + 7) / 8) * 8 * (d / 16);
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+#define GDN_COMBINE(D, SPL)                                                                             \
+    hipLaunchKernelGGL((seg_combine_kernel<D, SPL>), dim3((unsigned)blocks), dim3(4 * D), 0, stream, L, M, \
+                       Sstart, S_out, n_seqs, h_v, P)
     if (d == 128) {
-        hipLaunchKernelGGL(seg_combine_kernel<128>, dim3((unsigned)blocks), dim3(512), 0, stream, L, M, Sstart,
-                           S_out, n_seqs, h_v, P);
+        if (split) GDN_COMBINE(128, true);
+        else GDN_COMBINE(128, false);
     } else if (d == 64) {
-        hipLaunchKernelGGL(seg_combine_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, L, M, Sstart,
-                           S_out, n_seqs, h_v, P);
+        if (split) GDN_COMBINE(64, true);
+        else GDN_COMBINE(64, false);
     } else {
         return hipErrorNotSupported;
     }
+#undef GDN_COMBINE
     return hipGetLastError();
 }
 
