@@ -119,7 +119,7 @@ __global__ void __launch_bounds__(1024) seg_setup_kernel(const int32_t *cu, cons
 //     roundings leave ~2^-21 relative, against the 3e-3 tolerance of bf16 inputs): an
 //     eighth of the matrix-core cycles.  S is split once, when it is written to LDS.
 // Block: DK / 16 waves, one 16-row tile of the slice each; the M and L fragments of the
-// next two steps are in flight while the current step's products run.  S lives in LDS
+// next three steps are in flight while the current step's products run.  S lives in LDS
 // transposed ([column][row], rows padded so that the 16 lanes reading one k-range of
 // the 16 columns hit distinct banks), double-buffered across the steps.
 template <int DK, bool SPLIT>
@@ -154,27 +154,24 @@ __global__ void __launch_bounds__(64 * (DK / 16)) seg_combine_kernel(const float
     const int64_t SS = (int64_t)DK * DK;       // floats per state
     auto state_at = [&](int p) { return ((n * P + p) * h_v + h) * SS; };
     // this lane's part of S_new = M_p S + L_p: rows r0 + 4 (l/16) + i, column c0 + l%16.
-    // M_p fragments, row r0 + l%16: fp32, columns 16 kb + 4 (l/16) .. +3 of each 16-wide
-    // block; split, columns 32 j + 8 (l/16) .. +7 of each 32-wide block (the two halves
-    // of the same KB floats).  Two register sets keep the operands of steps p + 1 and
-    // p + 2 in flight while step p runs.
+    // M_p fragments, row r0 + l%16, columns 16 kb + 4 (l/16) .. +3 of each 16-wide block:
+    // each load reads one whole 1 KB tile.  The split products take the fragments of
+    // blocks 2 j and 2 j + 1 as the eight k values of one 16x16x32 product, i.e. lane
+    // group g contracts over columns 32 j + 4 g .. +3 and 32 j + 16 + 4 g .. +3 (the S
+    // fragments are read from LDS in the same order).  Three register sets keep the operands of steps p + 1 ..
+    // p + 3 in flight while step p runs; a set is refilled only once its step has consumed
+    // it, so the loop carries each set in the same registers (no copies that would wait
+    // for the loads just issued).
     struct Ops {
         f4 m[KB];
         f4 l;
     };
     auto load = [&](Ops &o, int p) {
         const int64_t base = state_at(p);
-        // (M is stored as 16 x 16 tiles: contiguous loads)
+        // (M is stored as 16 x 16 tiles)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            if constexpr (SPLIT) {   // 32-wide block kb/2, lane group l/16: 8 floats
-                const int t = 2 * (kb >> 1) + (lg >> 1);
-                o.m[kb] = *reinterpret_cast<const f4 *>(M + base + (int64_t)(wave * KB + t) * 256 + 16 * lr +
-                                                        8 * (lg & 1) + 4 * (kb & 1));
-            } else {
-                o.m[kb] = *reinterpret_cast<const f4 *>(M + base + (int64_t)(wave * KB + kb) * 256 + 16 * lr + 4 * lg);
-            }
-        }
+        for (int kb = 0; kb < KB; ++kb)
+            o.m[kb] = *reinterpret_cast<const f4 *>(M + base + (int64_t)(wave * KB + kb) * 256 + 16 * lr + 4 * lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) o.l[i] = L[base + (int64_t)(r0 + 4 * lg + i) * DK + c0 + lr];
     };
@@ -200,33 +197,35 @@ __global__ void __launch_bounds__(64 * (DK / 16)) seg_combine_kernel(const float
         *reinterpret_cast<f4 *>(dst + (int64_t)(r0 + lr) * DK + c0 + 4 * lg) = x;
     };
     int cur = 0;
-    // one step: the operands of step p + 2 into o, Sstart[v_p] = S, S = M_p S + L_p
+    // one step: Sstart[v_p] = S, S = M_p S + L_p, then the operands of step p + 3 into o
     auto step = [&](Ops &o, int p) {
-        f4 acc = o.l;
-        f4 m[KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) m[kb] = o.m[kb];
-        load(o, p + 2 < P ? p + 2 : P - 1);   // (unconditional: no branch around the loads)
-        // (the start state's store after the loads: a wait for those loads then never
-        // waits for this store's write as well)
         put_rows(Sstart + state_at(p), st[cur]);
+        f4 acc = o.l;
         if constexpr (SPLIT) {
+            h8 ah[KB / 2], al[KB / 2];
 #pragma unroll
             for (int j = 0; j < KB / 2; ++j) {
-                h8 ah, al;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float x = m[2 * j + (e >> 2)][e & 3];
-                    ah[e] = (_Float16)x;
-                    al[e] = (_Float16)(x - (float)ah[e]);
+                    const float x = o.m[2 * j + (e >> 2)][e & 3];
+                    ah[j][e] = (_Float16)x;
+                    al[j][e] = (_Float16)(x - (float)ah[j][e]);
                 }
-                const h8 bh = *reinterpret_cast<const h8 *>(&sth[cur][lr * LH + 32 * j + 8 * lg]);
-                const h8 bl = *reinterpret_cast<const h8 *>(&stl[cur][lr * LH + 32 * j + 8 * lg]);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc, 0, 0, 0);
             }
-            put_s(cur ^ 1, acc);
+#pragma unroll
+            for (int j = 0; j < KB / 2; ++j) {
+                typedef __attribute__((ext_vector_type(4))) _Float16 h4;
+                const int k0 = lr * LH + 32 * j + 4 * lg;
+                const h4 bh0 = *reinterpret_cast<const h4 *>(&sth[cur][k0]);
+                const h4 bh1 = *reinterpret_cast<const h4 *>(&sth[cur][k0 + 16]);
+                const h4 bl0 = *reinterpret_cast<const h4 *>(&stl[cur][k0]);
+                const h4 bl1 = *reinterpret_cast<const h4 *>(&stl[cur][k0 + 16]);
+                const h8 bh = __builtin_shufflevector(bh0, bh1, 0, 1, 2, 3, 4, 5, 6, 7);
+                const h8 bl = __builtin_shufflevector(bl0, bl1, 0, 1, 2, 3, 4, 5, 6, 7);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[j], bh, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[j], bl, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[j], bh, acc, 0, 0, 0);
+            }
         } else {
             // every S fragment first, then two independent product chains (even and odd
             // k-blocks), summed at the end
@@ -238,17 +237,21 @@ __global__ void __launch_bounds__(64 * (DK / 16)) seg_combine_kernel(const float
             for (int kb = 0; kb < KB; kb += 2) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(m[kb][j], bf[kb][j], acc, 0, 0, 0);
-                    acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(m[kb + 1][j], bf[kb + 1][j], acc2, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(o.m[kb][j], bf[kb][j], acc, 0, 0, 0);
+                    acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(o.m[kb + 1][j], bf[kb + 1][j], acc2, 0, 0, 0);
                 }
             }
-            put_s(cur ^ 1, acc + acc2);
+            acc += acc2;
         }
+        put_s(cur ^ 1, acc);
+        // (after the products: the registers of o, acc's start included, are free again;
+        // unconditional, no branch around the loads)
+        load(o, p + 3 < P ? p + 3 : P - 1);
         sync_lds();
         cur ^= 1;
     };
 
-    Ops A, B;
+    Ops A, B, C;
     // segment 0 starts from zero: S = L_0, no product
     {
         f4 z = {0.f, 0.f, 0.f, 0.f};
@@ -261,13 +264,20 @@ __global__ void __launch_bounds__(64 * (DK / 16)) seg_combine_kernel(const float
     }
     if (P > 1) {
         load(A, 1);
-        load(B, P > 2 ? 2 : 1);
+        load(B, P > 2 ? 2 : P - 1);
+        load(C, P > 3 ? 3 : P - 1);
     }
     sync_lds();
-    for (int p = 1; p < P; p += 2) {
+    // whole triples in the loop (every path round it runs all three steps, so the wait
+    // for a set's loads never has to assume the other two sets were skipped), then the rest
+    int p = 1;
+    for (; p + 2 < P; p += 3) {
         step(A, p);
-        if (p + 1 < P) step(B, p + 1);
+        step(B, p + 1);
+        step(C, p + 2);
     }
+    if (p < P) step(A, p);
+    if (p + 1 < P) step(B, p + 1);
     put_rows(S_out + (n * h_v + h) * SS, st[cur]);
 }
 
