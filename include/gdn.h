@@ -200,8 +200,10 @@ int32_t gdn_adaptive_replay_len_static(const gdn_desc *desc, const float *g,
  * recurrence; the pages replay one window per layer from a zero state).  Each window is
  * cut into P chunk-aligned segments of ceil(ceil(r/64)/P) chunks (trailing ones may be
  * empty); one launch forms every segment's S_local and M together, a combine chains
- * S_start(p+1) = M_p S_start(p) + S_local(p) from S_start(0) = 0 in fp32 and writes the
- * final state to S_out, and, when o_out is given, a second launch re-runs each segment
+ * S_start(p+1) = M_p S_start(p) + S_local(p) from S_start(0) = 0 with fp32 sums (bf16
+ * inputs: each fp32 operand as fp16 hi + lo halves, three products, about fp32 accuracy
+ * inside the fp16 range the bf16 path already requires) and writes the final state to
+ * S_out, and, when o_out is given, a second launch re-runs each segment
  * from its true start for the outputs (layouts as gdn_replay; cu_out likewise).
  * n_segments: P in [1, 64], or 0 for the library's choice, clamp(min(128 / (n_seqs h_v),
  * chunks / 6), 1, 16) with chunks = ceil(total_out_tokens / n_seqs / 64) when
