@@ -10,6 +10,7 @@ the whole window, so the tests see the decomposition and its arithmetic together
   * ragged windows (0, 1, 63, 64, 65, 200, 700 tokens) with grouped value heads, P larger
     than the chunk count of most windows (empty trailing segments), bf16 and fp32,
     d = 64 and 128, with outputs, state only, and the packed output offsets;
+  * P = 64 (the largest accepted; most segments empty), and 40 short sequences at P = 4;
   * P = 1 gives exactly gdn_replay (bit for bit): one segment's local state is the
     replayed state, its map multiplies a zero start;
   * an invalid device r is reported through the status word.
@@ -92,6 +93,30 @@ def test_ragged_windows(dtype, d, P):
     assert torch.equal(S, S2)
     # an empty window's state is exactly zero
     assert float(S[3].abs().max()) == 0.0
+
+
+def test_most_segments_and_many_sequences():
+    # P = 64, the largest accepted: most segments of these windows are empty, and the 448
+    # virtual sequences are more than the chunk kernel orders by length; then 40 sequences
+    # of mixed lengths at P = 4 (160 virtual sequences, ordered longest first)
+    rng = __import__("numpy").random.default_rng(99)
+    cases = [(W.small(W.config(1), RAGGED_L, RAGGED_R, h_qk=2, h_v=4, seed=6464), 64)]
+    Ls = [int(x) for x in rng.integers(1, 400, size=40)]
+    Rs = [int(rng.integers(0, L + 1)) for L in Ls]
+    cases.append((W.small(W.config(1), Ls, Rs, h_qk=1, h_v=2, seed=4040), 4))
+    for w, P in cases:
+        inp = W.make_inputs(w, device="cuda")
+        say("case", len(inp["r_host"]), "sequences, P", P)
+        S, o, cu_out = seg_run(inp, P)
+        torch.cuda.synchronize()
+        assert np.array_equal(cu_out.cpu().numpy(), np.concatenate([[0], np.cumsum(inp["r_host"])]))
+        host = dict(inp)
+        for key in ("q", "k", "v", "g", "beta"):
+            host[key] = inp[key].cpu()
+        S_ref, o_ref = oracle_run(host, "replay")
+        eS, eo = compare(host, "replay", S.cpu(), o.cpu(), S_ref, o_ref)
+        say("  relerr S %.3e  o %.3e" % (eS, eo))
+        assert eS <= TOL["bf16"] and eo <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
