@@ -517,25 +517,38 @@ __device__ __forceinline__ f32x4 tile_store(char *buf, float hr, float lr_, floa
                                             float scale) {
     const int lr = lane & 15, lg = lane >> 4;
     const int rr = 16 * ti + lr;
-    f32x4 av, pv;
+    f32x4 av, pv, ex;
+    // exp(H_i - H_j) of every entry, then a select: no divergent branch (the unused ones
+    // may be inf).  bf16 inputs: the gate row holds H log2(e), so one exp2 of the
+    // difference (its rounding, ~1e-5 relative under fast decay, is far below the bf16
+    // tolerance); fp32 inputs: the difference of the (hi, lo) pairs, then scaled.
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const int c = 16 * tj + 4 * lg + e;
-        // exp(H_i - H_j) of every entry, then a select: no divergent branch (the unused
-        // ones may be inf).  bf16 inputs: the gate row holds H log2(e), so one exp2 of
-        // the difference (its rounding, ~1e-5 relative under fast decay, is far below the
-        // bf16 tolerance); fp32 inputs: the difference of the (hi, lo) pairs, then scaled.
-        // Off-diagonal tiles (ti > tj, known when inlined) lie wholly below the diagonal.
-        float ex;
         if constexpr (P::kBF16) {
-            ex = __builtin_amdgcn_exp2f(hr - hc[e]);
+            ex[e] = __builtin_amdgcn_exp2f(hr - hc[e]);
         } else {
-            ex = __builtin_amdgcn_exp2f(((hr - hc[e]) + (lr_ - lc[e])) * 1.4426950408889634f);
+            ex[e] = __builtin_amdgcn_exp2f(((hr - hc[e]) + (lr_ - lc[e])) * 1.4426950408889634f);
         }
-        const bool below = ti > tj;
-        const float gam = ((below || c <= rr) && rho <= c) ? ex : 0.f;
-        av[e] = (below || c < rr) ? -br * gam * kk[e] : 0.f;
-        pv[e] = scale * gam * qk[e];
+    }
+    // Off-diagonal tiles (ti > tj, known when inlined) lie wholly below the diagonal; when
+    // in addition no row's last reset lies at or after the tile's first column (always, in
+    // a chunk without a reset), every entry is kept: one wave-wide test and a uniform
+    // branch instead of a compare and a select per entry
+    if (ti > tj && __builtin_amdgcn_ballot_w64(rho >= 16 * tj) == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            av[e] = -br * ex[e] * kk[e];
+            pv[e] = scale * ex[e] * qk[e];
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int c = 16 * tj + 4 * lg + e;
+            const bool below = ti > tj;
+            const float gam = ((below || c <= rr) && rho <= c) ? ex[e] : 0.f;
+            av[e] = (below || c < rr) ? -br * gam * kk[e] : 0.f;
+            pv[e] = scale * gam * qk[e];
+        }
     }
     if constexpr (P::kBF16) {
         const int eo = dt_index(ti, tj >> 1) * 1024 + 16 * lane + 8 * (tj & 1);
