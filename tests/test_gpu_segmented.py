@@ -11,6 +11,7 @@ the whole window, so the tests see the decomposition and its arithmetic together
     than the chunk count of most windows (empty trailing segments), bf16 and fp32,
     d = 64 and 128, with outputs, state only, and the packed output offsets;
   * P = 64 (the largest accepted; most segments empty), and 40 short sequences at P = 4;
+  * bf16 inputs with fp32 outputs and a non-unit output scale;
   * P = 1 gives exactly gdn_replay (bit for bit): one segment's local state is the
     replayed state, its map multiplies a zero start;
   * an invalid device r is reported through the status word.
@@ -35,7 +36,7 @@ def _gpu():
     yield
 
 
-def seg_run(inp, P, with_o=True, ws=None):
+def seg_run(inp, P, with_o=True, ws=None, o_dtype=None):
     import gated_deltanet_state_gdn_amd as gdn
     w = inp["workload"]
     tot = int(inp["r_host"].sum())
@@ -43,7 +44,7 @@ def seg_run(inp, P, with_o=True, ws=None):
     S, o, cu_out = gdn.gdn_replay_segmented(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
                                             inp["cu_seqlens"], inp["r"], total_out_tokens=tot,
                                             n_segments=P, o_out=True if with_o else None, cu_out=cu_out,
-                                            scale=w.scale, ws=ws)
+                                            scale=w.scale, ws=ws, o_dtype=o_dtype)
     return S, o, cu_out
 
 
@@ -117,6 +118,23 @@ def test_most_segments_and_many_sequences():
         eS, eo = compare(host, "replay", S.cpu(), o.cpu(), S_ref, o_ref)
         say("  relerr S %.3e  o %.3e" % (eS, eo))
         assert eS <= TOL["bf16"] and eo <= TOL["bf16"]
+
+
+def test_fp32_outputs_and_scale():
+    # bf16 inputs with fp32 outputs, and a non-unit output scale, through the output pass
+    w = W.small(W.config(1), [700, 90, 300], [650, 90, 129], h_qk=2, h_v=4, scale=0.125, seed=1250)
+    inp = W.make_inputs(w, device="cuda")
+    say("case bf16 inputs, fp32 outputs, scale 0.125, P 4")
+    S, o, cu_out = seg_run(inp, 4, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.float32
+    host = dict(inp)
+    for key in ("q", "k", "v", "g", "beta"):
+        host[key] = inp[key].cpu()
+    S_ref, o_ref = oracle_run(host, "replay")
+    eS, eo = compare(host, "replay", S.cpu(), o.cpu(), S_ref, o_ref)
+    say("  relerr S %.3e  o %.3e" % (eS, eo))
+    assert eS <= TOL["bf16"] and eo <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
