@@ -171,3 +171,21 @@ def test_segmented_workspace_bytes():
     assert gdn.gdn_segmented_workspace_bytes(d3, 0) == gdn.gdn_segmented_workspace_bytes(d3, 1)
     assert gdn.gdn_segmented_workspace_bytes(_desc(gdn, d_v=64), 4) == 0      # rejected descriptor
     assert gdn.gdn_segmented_workspace_bytes(d, 65) == 0
+
+
+def test_missing_library_fails_loudly():
+    # there is no fallback path: without the built library every call raises
+    import subprocess
+    import sys
+    code = ("import gated_deltanet_state_gdn_amd as gdn\n"
+            "try:\n"
+            "    gdn.load()\n"
+            "except ImportError as e:\n"
+            "    print('raised:', e)\n"
+            "else:\n"
+            "    raise SystemExit('loaded without a library')\n")
+    env = dict(os.environ, GDN_LIB_PATH=os.path.join(ROOT, "no_such_dir", "libgdn.so"))
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                         timeout=120)
+    assert out.returncode == 0, out.stderr
+    assert "raised:" in out.stdout and "not built" in out.stdout
