@@ -109,7 +109,7 @@ int32_t run(const gdn_desc *d, const void *q, const void *k, const void *v, cons
 // word -- virtual cu_seqlens, virtual r, the map launch's states (S_local and M of every
 // segment), every segment's true start state.
 // The default: enough segments that the map launch and the output launch each fill about
-// half the chip (128 / (n_seqs h_v)), but at least ~6 chunks per segment, judged from the
+// half the chip (128 / (n_seqs h_v)), but at least ~6 chunks per segment, estimated from the
 // mean replay length total_out_tokens / n_seqs when it is given (measured: shorter segments
 // cost more in the extra launches and the combine than they save).
 int32_t seg_count(const gdn_desc *d, int32_t n_segments)
