@@ -1237,7 +1237,11 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         // rows and its LDS slots (a bf16 unit is logical chunks c0 and c0 + 1 of a row; the
         // lanes of the upper half of a row write them in the other order, so that each
         // store's eight lanes of one row hit eight distinct 16-byte slots modulo 128 bytes,
-        // the stores' bank rule)
+        // the stores' bank rule).  The column-slice variant with helper waves keeps the plain
+        // order: with one state wave per slice the LDS is lightly loaded, and the register
+        // selects the swap costs sit on the preparation chain that paces such a slice
+        // (measured: the 8K and slow-decay layers 1.4 and 2.1 % faster this way; without
+        // the swap in every variant the stack was 0.3 % slower, so the whole-unit one keeps it)
         const int spt = 64 * pw + fresh_lane();
         const bool s_act = UT >= TH || spt < UT;   // with fewer units than threads, the last waves idle
         const int spu = spt % NPU, srow = spt / NPU;
@@ -1254,7 +1258,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         const int spuv = 2 * ((c_lo - cb * W) >> 5) + (spt & (nuv - 1));
         const bool v_act = STAGE_V && srowv < CH;
         const uint32_t v_vo = (uint32_t)srowv * vrowp + (uint32_t)(64 * (spuv >> 1) + 16 * (spuv & 1));
-        const bool v_sw = (spuv & 4) != 0;
+        const bool v_sw = !HELP && (spuv & 4) != 0;
         int v_oa = 0, v_ob = 0;
         if constexpr (STAGE_V) {
             const int c0 = 4 * (spuv >> 1) + 2 * (spuv & 1);
@@ -1263,7 +1267,7 @@ __global__ void __launch_bounds__(64 * (W / 16 + NPW)) gdn_chunk_ws_kernel(Chunk
         }
         const uint32_t s_vo = (uint32_t)srow * krow +
                               (uint32_t)(P::kBF16 ? 64 * (spu >> 1) + 16 * (spu & 1) : 16 * spu);
-        const bool s_sw = P::kBF16 && (spu & 4) != 0;
+        const bool s_sw = P::kBF16 && !HELP && (spu & 4) != 0;
         int s_oa[NR], s_ob[NR];
 #pragma unroll
         for (int j = 0; j < NR; ++j) {
