@@ -11,6 +11,7 @@ the whole window, so the tests see the decomposition and its arithmetic together
     than the chunk count of most windows (empty trailing segments), bf16 and fp32,
     d = 64 and 128, with outputs, state only, and the packed output offsets;
   * P = 64 (the largest accepted; most segments empty), and 40 short sequences at P = 4;
+  * one stack layer (32 v heads over 16 q/k heads, r = 3277) at 4 segments, every head;
   * bf16 inputs with fp32 outputs and a non-unit output scale;
   * P = 1 gives exactly gdn_replay (bit for bit): one segment's local state is the
     replayed state, its map multiplies a zero start;
@@ -118,6 +119,23 @@ def test_most_segments_and_many_sequences():
         eS, eo = compare(host, "replay", S.cpu(), o.cpu(), S_ref, o_ref)
         say("  relerr S %.3e  o %.3e" % (eS, eo))
         assert eS <= TOL["bf16"] and eo <= TOL["bf16"]
+
+
+def test_stack_layer_shape_all_heads():
+    # one layer of the 36-layer stack (16 q/k heads shared by 32 v heads, L = 32768,
+    # r = 3277) at 4 segments, the call and segment count the benchmark times; every head
+    w = W.config(2).with_(layers=1)
+    inp = W.make_inputs(w, device="cuda")
+    say("case", w.name, "one layer, segmented replay P=4")
+    S, o, cu_out = seg_run(inp, 4)
+    torch.cuda.synchronize()
+    host = dict(inp)
+    for key in ("q", "k", "v", "g", "beta"):
+        host[key] = inp[key].cpu()
+    S_ref, o_ref = oracle_run(host, "replay")
+    eS, eo = compare(host, "replay", S.cpu(), o.cpu(), S_ref, o_ref)
+    say("  relerr S %.3e  o %.3e" % (eS, eo))
+    assert eS <= TOL["bf16"] and eo <= TOL["bf16"]
 
 
 def test_fp32_outputs_and_scale():
