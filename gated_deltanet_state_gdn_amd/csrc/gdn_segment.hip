@@ -115,8 +115,8 @@ __global__ void __launch_bounds__(1024) seg_setup_kernel(const int32_t *cu, cons
 //   SPLIT = false: 16x16x4 fp32 products (exact products), for fp32 inputs.
 //   SPLIT = true (bf16 inputs, whose state is bounded by the fp16 range contract): every
 //     operand x is split into fp16 hi = fp16(x) and lo = fp16(x - hi), and M S is formed
-//     as hi*hi + hi*lo + lo*hi on 16x16x32 fp16 products: an eighth of the matrix-core
-//     cycles.  The dropped lo*lo and the roundings leave ~2e-7 of the step's result
+//     as hi*hi + hi*lo + lo*hi on 16x16x32 fp16 products: three matrix instructions per
+//     32-wide k-block instead of eight 16x16x4 fp32 ones.  The dropped lo*lo and the roundings leave ~2e-7 of the step's result
 //     M S + L, as an fp32 product would, also for decayed maps whose small entries have
 //     fp16-subnormal lo halves (an absolute error of 2^-25 per entry, small against L).
 //     S is split once, when it is written to LDS.
